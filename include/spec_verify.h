@@ -1,0 +1,146 @@
+/* spec_verify.h - C ABI of the gfx950 (MI355X) speculative-sampling verify step.
+ *
+ * The verify step of speculative decoding: given the target model's logits at
+ * K+1 positions and the draft model's logits at K positions over the whole
+ * vocabulary, together with the K draft tokens, decide how many draft tokens
+ * survive and which token ends the round.  Sources, cited by page and section:
+ *
+ *   [QH] quochung.cyou, "A.I" category page, speculative decoding tutorial:
+ *        "Chọn token: greedy vs sampling" (greedy = most likely token;
+ *        sampling = draw in proportion), "Một vòng speculative decoding" and
+ *        "Draft model kém hơn target..." (greedy verify, left-to-right
+ *        comparison, the tail after a mismatch is dropped unchecked),
+ *        "Modified rejection sampling" with "Giải pháp" (acceptance
+ *        probability min(1, p/q)), "Khi reject thì lấy token từ đâu?"
+ *        (correction from the normalised residual max(0, p - q)), "Toàn bộ
+ *        thuật toán cho một token" and "Áp dụng thuật toán" (first rejection
+ *        ends the round; all K accepted -> one bonus token from the target).
+ *   [NL] nalar.dev, "Speculative decoding: memverifikasi token draft secara
+ *        paralel": "Sampling eksak memerlukan aturan koreksi" (a(x) and the
+ *        residual r(x)), "Penolakan memotong prefix yang diterima" (a
+ *        rejection truncates the accepted prefix).
+ *   [MC] ml-canon-ru card 57 "Speculative Decoding": "Приёмка и почему
+ *        распределение НЕ портится" (alpha, the residual, the exactness
+ *        identity) and its sketch of one round (strict u < alpha).
+ *
+ * Conventions fixed here where the pages leave a step open:
+ *   - p = softmax(target_logits / T), q = softmax(draft_logits / T), T > 0.
+ *   - Test j (j < K) accepts draft token x_j iff u[b,j] * q_j(x_j) < p_j(x_j),
+ *     i.e. u < min(1, p/q) with q(x) = 0 meaning alpha = 1 if p(x) > 0, else 0.
+ *   - The one final draw uses u[b,K] by inverse CDF over ascending token
+ *     index: the smallest i whose running sum of the weights exceeds u * S.
+ *     Weights: max(0, p_n - q_n) after a rejection at n (p_n if that sum
+ *     rounds to 0), or p_K for the bonus token.
+ *   - Greedy sequences: accept x_j iff it equals the lowest-index argmax of the
+ *     raw target logits of row j; the final token is that argmax of row n.
+ *     They ignore temperature, uniforms and draft logits.
+ *
+ * Memory: every array argument is a DEVICE pointer owned by the caller,
+ * row-major and contiguous, aligned to its element size (16-byte-aligned rows
+ * take the vector path; other rows are still handled).  The library
+ * allocates and frees nothing.  All calls are asynchronous on `stream` (a
+ * hipStream_t; NULL = the default stream) and return after enqueueing.
+ *
+ * Errors: 0 = OK.  Negative codes are host-detected and nothing is launched:
+ *   SV_EINVAL    shape out of range (B < 0, K not in [0, SV_MAX_K], V < 1),
+ *                unknown dtype, temperature not finite and > 0, a required
+ *                pointer NULL or misaligned, grid too large.
+ *   SV_EWORKSPACE workspace NULL, misaligned (16 B) or smaller than
+ *                sv_workspace_bytes().
+ *   SV_ELAUNCH   the HIP launch failed.
+ * Per-sequence input faults are reported on the device: a row the method
+ * examines that holds NaN or +Inf or is all -Inf, a token outside [0, V), a
+ * uniform outside [0, 1) that the method uses, or a sampling sequence with
+ * draft_logits == NULL gives accepted_len[b] = -1 and out_tokens[b,:] = -1;
+ * other sequences are unaffected.  -Inf logits are legal (masked tokens).
+ * Rows past the first rejection never change the result.
+ *
+ * Determinism: identical inputs give bitwise-identical outputs.
+ * Concurrency: calls that share a workspace must be ordered on one stream.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_F32  0   /* fp32 logits */
+#define SV_BF16 1   /* bf16 logits (uint16 storage) */
+
+#define SV_OK          0
+#define SV_EINVAL     -1
+#define SV_EWORKSPACE -2
+#define SV_ELAUNCH    -3
+
+#define SV_MAX_K 63
+
+/* Optional diagnostics: a host struct of device pointers, each may be NULL.
+ * Entries the method never examines (positions after the first rejection,
+ * greedy sequences, invalid sequences) are NaN.                              */
+typedef struct sv_diag {
+    float* p_tok;     /* [B,K]   p_j(x_j) at tested positions j <= n          */
+    float* q_tok;     /* [B,K]   q_j(x_j) at tested positions                 */
+    float* lse_p;     /* [B,K+1] ln sum_i exp(l_i/T) for target rows j <= n   */
+    float* lse_q;     /* [B,K]   same for draft rows j <= min(n, K-1)         */
+    float* res_mass;  /* [B]     S of the final draw in probability units:
+                                 sum max(0, p_n - q_n), ~1 for the bonus,
+                                 0 for greedy, 0 if the residual fell back    */
+} sv_diag;
+
+/* Bytes of device workspace spec_verify needs for this shape (0 for B == 0).
+ * The workspace must be zero-filled once when allocated; every completed
+ * call leaves its counters at zero again, so it can be reused as is.         */
+size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype);
+
+/* The whole verify step (steps: row statistics, acceptance tests, first
+ * rejection, final draw, emit).
+ *   target_logits [B, K+1, V] dtype    draft_logits [B, K, V] dtype (may be
+ *   NULL when K == 0 or every sequence is greedy)
+ *   draft_tokens  [B, K] int32 (NULL allowed only when K == 0)
+ *   uniforms      [B, K+1] fp32 in [0,1): column j < K tests position j,
+ *                 column K drives the final draw
+ *   temperature   shared by p and q
+ *   greedy_flag   [B] uint8, 1 = greedy sequence; NULL = all sampling
+ * Outputs:
+ *   accepted_len  [B] int32: n in [0, K] accepted draft tokens, -1 = invalid
+ *   out_tokens    [B, K+1] int32: x_0..x_{n-1}, then the correction or bonus
+ *                 token, then -1 padding.                                    */
+int spec_verify(const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, const float* uniforms,
+                float temperature, const uint8_t* greedy_flag,
+                int32_t B, int32_t K, int32_t V, int32_t dtype,
+                int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same call split in its two launches, for timing and for checking the
+ * split against the whole: sv_stats streams every row once and settles n,
+ * the accepted prefix and greedy results; sv_draw makes the final draw of
+ * sampling sequences.  sv_draw must follow sv_stats on the same stream with
+ * identical arguments.                                                       */
+int sv_stats(const void* target_logits, const void* draft_logits,
+             const int32_t* draft_tokens, const float* uniforms,
+             float temperature, const uint8_t* greedy_flag,
+             int32_t B, int32_t K, int32_t V, int32_t dtype,
+             int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+             void* workspace, size_t workspace_bytes, void* stream);
+int sv_draw(const void* target_logits, const void* draft_logits,
+            const int32_t* draft_tokens, const float* uniforms,
+            float temperature, const uint8_t* greedy_flag,
+            int32_t B, int32_t K, int32_t V, int32_t dtype,
+            int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Short text for a return code (static storage). */
+const char* sv_strerror(int code);
+
+/* ABI version of this header: 1. */
+int sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

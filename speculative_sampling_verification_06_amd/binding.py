@@ -1,0 +1,214 @@
+"""Thin Python binding of libspecverify.so (argument marshalling only).
+
+Every step of the verify path runs in the HIP kernels behind the C ABI in
+include/spec_verify.h.  torch supplies device memory and the stream; this
+module only checks shapes and dtypes, passes data pointers and the current
+stream, and keeps one zero-initialised workspace per device.  There is no
+CPU fallback: if the library is missing or no GPU is present, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_ELAUNCH = 0, -1, -2, -3
+SV_MAX_K = 63
+
+# The exported names, as declared in include/spec_verify.h.
+EXPORTS = ("sv_workspace_bytes", "spec_verify", "sv_stats", "sv_draw", "sv_strerror", "sv_version")
+
+
+class SvDiag(C.Structure):
+    _fields_ = [("p_tok", C.c_void_p), ("q_tok", C.c_void_p), ("lse_p", C.c_void_p),
+                ("lse_q", C.c_void_p), ("res_mass", C.c_void_p)]
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (no GPU needed to load it)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build it with "
+                    "`python -m speculative_sampling_verification_06_amd.build`")
+            lib = C.CDLL(path)
+            verify_args = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_void_p,
+                           C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                           C.POINTER(SvDiag), C.c_void_p, C.c_size_t, C.c_void_p]
+            for name in ("spec_verify", "sv_stats", "sv_draw"):
+                fn = getattr(lib, name)
+                fn.restype = C.c_int
+                fn.argtypes = verify_args
+            lib.sv_workspace_bytes.restype = C.c_size_t
+            lib.sv_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+            lib.sv_strerror.restype = C.c_char_p
+            lib.sv_strerror.argtypes = [C.c_int]
+            lib.sv_version.restype = C.c_int
+            lib.sv_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().sv_strerror(int(code)).decode()
+
+
+def workspace_bytes(B: int, K: int, V: int, dtype: int) -> int:
+    return int(load_library().sv_workspace_bytes(B, K, V, dtype))
+
+
+# ------------------------------------------------------------------ torch --
+
+def _torch():
+    import torch
+    return torch
+
+
+_ws_cache: dict = {}
+
+
+def get_workspace(nbytes: int, device):
+    """A zero-filled workspace of at least nbytes on `device`, reused across calls.
+
+    The kernels leave its counters at zero after every completed call, so it
+    is zeroed once, when allocated.
+    """
+    torch = _torch()
+    key = (str(device),)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev_ptr(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr() if t.numel() else None
+
+
+class Outputs(dict):
+    __getattr__ = dict.__getitem__
+
+
+def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
+          outputs=None, diag=True, workspace=None, stream=None):
+    torch = _torch()
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target logits must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _dtype_code(target)
+    dev = target.device
+    _dev_ptr(target, "target_logits", shape=(B, K + 1, V))
+    if draft is not None:
+        if draft.dtype != target.dtype:
+            raise TypeError("draft logits must have the target's dtype")
+        _dev_ptr(draft, "draft_logits", shape=(B, K, V))
+    if tokens is not None:
+        _dev_ptr(tokens, "draft_tokens", torch.int32, (B, K))
+    _dev_ptr(uniforms, "uniforms", torch.float32, (B, K + 1))
+    if greedy is not None:
+        _dev_ptr(greedy, "greedy_flag", torch.uint8, (B,))
+    if outputs is None:
+        outputs = Outputs(
+            accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+            out_tokens=torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+        if diag:
+            outputs.update(
+                p_tok=torch.empty(B, K, dtype=torch.float32, device=dev),
+                q_tok=torch.empty(B, K, dtype=torch.float32, device=dev),
+                lse_p=torch.empty(B, K + 1, dtype=torch.float32, device=dev),
+                lse_q=torch.empty(B, K, dtype=torch.float32, device=dev),
+                res_mass=torch.empty(B, dtype=torch.float32, device=dev))
+    dg = None
+    if "p_tok" in outputs:
+        dg = SvDiag(*[_dev_ptr(outputs[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
+    need = lib.sv_workspace_bytes(B, K, V, dt)
+    ws = workspace if workspace is not None else get_workspace(need, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = getattr(lib, fn_name)(
+        target.data_ptr(), None if draft is None else draft.data_ptr(),
+        None if tokens is None or tokens.numel() == 0 else tokens.data_ptr(),
+        uniforms.data_ptr(), C.c_float(float(temperature)),
+        None if greedy is None else greedy.data_ptr(), B, K, V, dt,
+        _dev_ptr(outputs["accepted_len"], "accepted_len", torch.int32, (B,)),
+        _dev_ptr(outputs["out_tokens"], "out_tokens", torch.int32, (B, K + 1)),
+        None if dg is None else C.byref(dg), ws.data_ptr(), ws.numel(), stream)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+    return outputs
+
+
+def verify(target, draft, tokens, uniforms, temperature, greedy=None, **kw):
+    """spec_verify on torch device tensors -> Outputs(accepted_len, out_tokens[, diagnostics])."""
+    return _call("spec_verify", target, draft, tokens, uniforms, temperature, greedy, **kw)
+
+
+def stats(target, draft, tokens, uniforms, temperature, greedy=None, **kw):
+    """First launch only (row statistics, tests, first rejection, greedy results)."""
+    return _call("sv_stats", target, draft, tokens, uniforms, temperature, greedy, **kw)
+
+
+def draw(target, draft, tokens, uniforms, temperature, greedy=None, **kw):
+    """Second launch only (final draw of sampling sequences); pass stats()'s outputs."""
+    return _call("sv_draw", target, draft, tokens, uniforms, temperature, greedy, **kw)
+
+
+def to_device(w, device="cuda:0"):
+    """Copy a host Workload's arrays to device tensors (bf16 bits become torch.bfloat16)."""
+    torch = _torch()
+    import numpy as np
+
+    def logits(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        if a.dtype == np.float32:
+            return torch.from_numpy(a).to(device)
+        raise TypeError(f"unsupported logit storage {a.dtype} for the device path")
+
+    return dict(
+        target=logits(w.target) if w.target.size else None,
+        draft=logits(w.draft) if w.K > 0 else None,
+        tokens=torch.from_numpy(np.ascontiguousarray(w.tokens, np.int32)).to(device),
+        uniforms=torch.from_numpy(np.ascontiguousarray(w.uniforms, np.float32)).to(device),
+        greedy=torch.from_numpy(np.ascontiguousarray(w.greedy, np.uint8)).to(device),
+        temperature=float(w.T))

@@ -1,0 +1,917 @@
+// spec_verify.hip - gfx950 (MI355X) kernels and C ABI of the speculative-sampling
+// verify step.  Page citations ([QH], [NL], [MC]) are spelled out in
+// include/spec_verify.h next to the declarations.
+//
+// Two launches, both HBM streams:
+//
+//   k_stats  one workgroup per (sequence b, row r, vocab chunk c).  Rows
+//            r = 0..K are target rows, r = K+1..2K draft rows.  The chunk is
+//            streamed once with 16-byte loads (UNROLL of them in flight per
+//            lane); sampling rows keep an online softmax state (running max m
+//            and sum z of exp2(x*s - m*s), s = log2(e)/T), greedy rows keep a
+//            lowest-index argmax.  The partial goes to the workspace; the last
+//            workgroup of the sequence to arrive (self-resetting atomic
+//            counter) merges the partials in a fixed order, evaluates the K
+//            acceptance tests on wave 0, finds the first rejection with one
+//            64-lane ballot, writes the accepted prefix and the greedy result
+//            and records what the draw needs.
+//   k_draw   one workgroup per (sampling sequence b, tile of row n).  Each
+//            wave sums the draw weights (residual max(0, p - q) scaled by Z_p,
+//            or p for the bonus) over 64*E-element segments; the last tile to
+//            arrive scans the segment sums, re-reads the one segment that
+//            holds u*S, scans it lane by lane and writes the final token.
+//
+// Numerics: every term is exp2(fma(x, s, -c)) with c = m*s held as an exact
+// shift, so the row's own rounding of c cancels out of every ratio; partial
+// states are merged by rescaling with exp2(c_i - c).  Sums are fp32 trees
+// (window, wave butterfly, fixed-order merges), never float atomics, so the
+// result is bitwise deterministic.  The max is NaN-propagating, so a NaN
+// anywhere in a row turns its sum into NaN and the row is reported invalid.
+
+#include <hip/hip_runtime.h>
+
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+constexpr int NT = 256;               // threads per workgroup: four wave64
+constexpr int NWAVE = NT / 64;
+constexpr int UNROLL = 4;             // 16-byte loads in flight per lane and row
+constexpr int SPW = 4;                // draw: segments per wave per tile
+constexpr int SPT = NWAVE * SPW;      // draw: segments per tile
+constexpr int MAXR = 2 * SV_MAX_K + 1;
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float POS_INF = __builtin_inff();
+constexpr float LN2 = 0.693147180559945309417f;
+
+template <int DT> struct Fmt;
+template <> struct Fmt<SV_F32> {
+    static constexpr int E = 4, BYTES = 4;
+    static constexpr uint32_t NEG_INF_WORD = 0xff800000u;
+};
+template <> struct Fmt<SV_BF16> {
+    static constexpr int E = 8, BYTES = 2;
+    static constexpr uint32_t NEG_INF_WORD = 0xff80ff80u;
+};
+
+struct Partial {      // one (row, chunk): softmax {m, z} or argmax {m = value, idx, bad}
+    float m;
+    float z;
+    int32_t idx;
+    uint32_t bad;
+};
+
+struct SeqRec {       // what k_stats leaves for k_draw
+    int32_t n;
+    int32_t status;   // 1 = sampling sequence, valid, draw pending
+    float mp, zp;     // target row n
+    float mq, zq;     // draft row n (n < K)
+    float u;          // uniforms[b, K]
+    int32_t pad;
+};
+
+struct Params {
+    const void* target;
+    const void* draft;
+    const int32_t* tokens;
+    const float* uniforms;
+    const uint8_t* greedy;
+    int32_t* acc;
+    int32_t* out;
+    float* p_tok;
+    float* q_tok;
+    float* lse_p;
+    float* lse_q;
+    float* res_mass;
+    Partial* part;
+    SeqRec* rec;
+    uint32_t* cnt1;
+    uint32_t* cnt2;
+    float* seg;       // [2][B][nseg]: residual sums, then p sums
+    int32_t B, K, V, C;
+    int32_t nseg, tiles;
+    float s;          // log2(e) / T
+};
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float shift_of(float m, float s) { return m == NEG_INF ? 0.f : m * s; }
+
+template <int N>
+__device__ __forceinline__ float tree_max(const float* x)
+{
+    if constexpr (N == 1) {
+        return x[0];
+    } else if constexpr (N == 2) {
+        return vmax(x[0], x[1]);
+    } else {
+        constexpr int M = (N + 2) / 3;
+        float a[M];
+#pragma unroll
+        for (int k = 0; k < N / 3; ++k) a[k] = vmax(vmax(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
+        if constexpr (N % 3 == 1) a[N / 3] = x[N - 1];
+        if constexpr (N % 3 == 2) a[N / 3] = vmax(x[N - 2], x[N - 1]);
+        return tree_max<M>(a);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float tree_sum(float* t)
+{
+    if constexpr (N == 1) {
+        return t[0];
+    } else {
+        constexpr int H = N / 2;
+#pragma unroll
+        for (int k = 0; k < H; ++k) t[k] = t[k] + t[k + (N - H)];
+        return tree_sum<N - H>(t);
+    }
+}
+
+template <int DT> __device__ __forceinline__ void unpack(const uint4& v, float* x);
+template <> __device__ __forceinline__ void unpack<SV_F32>(const uint4& v, float* x)
+{
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+}
+template <> __device__ __forceinline__ void unpack<SV_BF16>(const uint4& v, float* x)
+{
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xffff0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xffff0000u);
+    x[4] = __uint_as_float(v.z << 16);
+    x[5] = __uint_as_float(v.z & 0xffff0000u);
+    x[6] = __uint_as_float(v.w << 16);
+    x[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+template <int DT>
+__device__ __forceinline__ float load1(const char* row, int64_t i)
+{
+    if constexpr (DT == SV_F32) return reinterpret_cast<const float*>(row)[i];
+    else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
+}
+
+// E consecutive elements starting at e (a multiple of E); -inf past V.
+template <int DT>
+__device__ __forceinline__ void load_elems(const char* row, int64_t e, int64_t V, bool aligned, float* x)
+{
+    constexpr int E = Fmt<DT>::E;
+    if (aligned && e + E <= V) {
+        uint4 v = *reinterpret_cast<const uint4*>(row + e * Fmt<DT>::BYTES);
+        unpack<DT>(v, x);
+    } else {
+#pragma unroll
+        for (int k = 0; k < E; ++k) x[k] = (e + k < V) ? load1<DT>(row, e + k) : NEG_INF;
+    }
+}
+
+// ------------------------------------------------- online softmax / argmax --
+
+struct SmState { float m, z; };
+struct AmState { float v; int32_t i; uint32_t bad; };
+
+__device__ __forceinline__ SmState sm_merge(SmState a, SmState b, float s)
+{
+    const float mn = vmax(a.m, b.m);
+    const float cn = shift_of(mn, s);
+    const float fa = (a.m == NEG_INF) ? 0.f : ex2(shift_of(a.m, s) - cn);
+    const float fb = (b.m == NEG_INF) ? 0.f : ex2(shift_of(b.m, s) - cn);
+    return {mn, __builtin_fmaf(a.z, fa, b.z * fb)};
+}
+
+__device__ __forceinline__ AmState am_merge(AmState a, AmState b)
+{
+    AmState r = (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+    r.bad = a.bad | b.bad;
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ void sm_window(const float* x, float s, SmState& st)
+{
+    const float wm = tree_max<N>(x);
+    const float mn = vmax(st.m, wm);
+    const float cn = shift_of(mn, s);
+    const float sc = (st.m == NEG_INF) ? 0.f : ex2(shift_of(st.m, s) - cn);
+    float t[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) t[k] = ex2(__builtin_fmaf(x[k], s, -cn));
+    const float ws = tree_sum<N>(t);
+    st.z = __builtin_fmaf(st.z, sc, ws);
+    st.m = mn;
+}
+
+// idx(k) gives the row index of x[k]; increasing in k.
+template <int N, typename IdxF>
+__device__ __forceinline__ void am_window(const float* x, IdxF idx, AmState& st)
+{
+    const float wm = tree_max<N>(x);
+    if (wm != wm || wm == POS_INF) st.bad = 1u;
+    if (wm > st.v) {
+        int kk = N - 1;
+#pragma unroll
+        for (int k = N - 1; k >= 0; --k)
+            if (x[k] == wm) kk = k;
+        st.v = wm;
+        st.i = (int32_t)idx(kk);
+    }
+}
+
+// Stream elements [e0, e1) of one row (e0 a multiple of E) into the state.
+template <int DT, bool GREEDY>
+__device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t e1, float s,
+                                           SmState& sm, AmState& am)
+{
+    constexpr int E = Fmt<DT>::E;
+    constexpr int W = UNROLL * E;
+    const int tid = threadIdx.x;
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    if (aligned) {
+        const uint4* vrow = reinterpret_cast<const uint4*>(row);
+        const int64_t v0 = e0 / E, v1 = e1 / E;
+        for (int64_t base = v0 + tid; base < v1; base += (int64_t)NT * UNROLL) {
+            uint4 raw[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t vi = base + (int64_t)u * NT;
+                if (vi < v1) raw[u] = vrow[vi];
+                else raw[u] = make_uint4(Fmt<DT>::NEG_INF_WORD, Fmt<DT>::NEG_INF_WORD,
+                                         Fmt<DT>::NEG_INF_WORD, Fmt<DT>::NEG_INF_WORD);
+            }
+            float x[W];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) unpack<DT>(raw[u], x + u * E);
+            if constexpr (GREEDY)
+                am_window<W>(x, [base](int k) { return (base + (int64_t)(k / E) * NT) * E + (k % E); }, am);
+            else
+                sm_window<W>(x, s, sm);
+        }
+        const int64_t t0 = v1 * E;             // ragged tail of the row (< E elements)
+        if (t0 + tid < e1) {
+            float x1[1] = {load1<DT>(row, t0 + tid)};
+            const int64_t i1 = t0 + tid;
+            if constexpr (GREEDY) am_window<1>(x1, [i1](int) { return i1; }, am);
+            else sm_window<1>(x1, s, sm);
+        }
+    } else {
+        for (int64_t base = e0 + tid; base < e1; base += (int64_t)NT * W) {
+            float x[W];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int64_t i = base + (int64_t)k * NT;
+                x[k] = (i < e1) ? load1<DT>(row, i) : NEG_INF;
+            }
+            if constexpr (GREEDY)
+                am_window<W>(x, [base](int k) { return base + (int64_t)k * NT; }, am);
+            else
+                sm_window<W>(x, s, sm);
+        }
+    }
+}
+
+// ------------------------------------------------------- block reductions --
+
+__device__ __forceinline__ SmState block_reduce_sm(SmState v, float s, SmState* sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        SmState o = {__shfl_xor(v.m, off, 64), __shfl_xor(v.z, off, 64)};
+        v = sm_merge(v, o, s);
+    }
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    SmState r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) r = sm_merge(r, sh[w], s);
+    return r;
+}
+
+__device__ __forceinline__ AmState block_reduce_am(AmState v, AmState* sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        AmState o = {__shfl_xor(v.v, off, 64), __shfl_xor(v.i, off, 64),
+                     (uint32_t)__shfl_xor((int)v.bad, off, 64)};
+        v = am_merge(v, o);
+    }
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    AmState r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) r = am_merge(r, sh[w]);
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_incl_scan(float v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(v, off, 64);
+        if (lane >= off) v += y;
+    }
+    return v;
+}
+
+// Inclusive scan over the workgroup; *total gets the sum of all NT values.
+__device__ __forceinline__ float block_incl_scan(float v, float* sh, float* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_incl_scan(v);
+    if (lane == 63) sh[wave] = v;
+    __syncthreads();
+    float off = 0.f, tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+        if (w < wave) off += sh[w];
+        tot += sh[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return v + off;
+}
+
+// Arrival on a per-sequence counter that wraps back to zero after `total`
+// arrivals.  Returns true in the last workgroup to arrive, after an acquire.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, int* sh_flag)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();                                   // release this group's writes
+        const uint32_t old = atomicInc(counter, total - 1u);
+        *sh_flag = (old == total - 1u);
+    }
+    __syncthreads();
+    const bool last = *sh_flag != 0;
+    if (last) __threadfence();                             // acquire everyone else's
+    return last;
+}
+
+template <int DT>
+__device__ __forceinline__ const char* target_row(const Params& P, int b, int j)
+{
+    return reinterpret_cast<const char*>(P.target) +
+           ((int64_t)b * (P.K + 1) + j) * (int64_t)P.V * Fmt<DT>::BYTES;
+}
+template <int DT>
+__device__ __forceinline__ const char* draft_row(const Params& P, int b, int j)
+{
+    return reinterpret_cast<const char*>(P.draft) +
+           ((int64_t)b * P.K + j) * (int64_t)P.V * Fmt<DT>::BYTES;
+}
+
+__device__ __forceinline__ void put(float* a, int64_t i, float v) { if (a) a[i] = v; }
+
+// ---------------------------------------------- stats: settle n per sequence --
+
+template <int DT>
+__device__ void finalize_seq(const Params& P, int b, bool greedy)
+{
+    const int K = P.K, V = P.V, C = P.C, R = 2 * K + 1;
+    const float s = P.s;
+    const int tid = threadIdx.x;
+    __shared__ float f_m[MAXR], f_z[MAXR];
+    __shared__ int32_t f_i[MAXR];
+    __shared__ int32_t f_ok[MAXR];
+
+    // merge the C chunk partials of every row, in chunk order
+    if (tid < R) {
+        const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
+        if (greedy) {
+            if (tid <= K) {
+                AmState a = {NEG_INF, INT_MAX, 0u};
+                for (int c = 0; c < C; ++c) a = am_merge(a, {pp[c].m, pp[c].idx, pp[c].bad});
+                f_m[tid] = a.v;
+                f_i[tid] = a.i;
+                f_ok[tid] = (a.bad == 0u) && a.v > NEG_INF && a.v < POS_INF;
+            } else {
+                f_ok[tid] = 0;
+            }
+        } else if (tid <= K || P.draft != nullptr) {
+            SmState a = {NEG_INF, 0.f};
+            for (int c = 0; c < C; ++c) a = sm_merge(a, {pp[c].m, pp[c].z}, s);
+            f_m[tid] = a.m;
+            f_z[tid] = a.z;
+            f_ok[tid] = (a.z > 0.f) && (a.z < POS_INF) && a.m > NEG_INF && a.m < POS_INF;
+        } else {
+            f_ok[tid] = 0;
+        }
+    }
+    __syncthreads();
+    if (tid >= 64) return;                              // wave 0 decides; no barrier below
+
+    const int j = tid;
+    const int64_t ub = (int64_t)b * (K + 1);
+    bool stop = false, inval = false;
+    float ptok = NAN, qtok = NAN;
+    int32_t x = -1;
+    if (j < K) {
+        x = P.tokens[(int64_t)b * K + j];
+        const bool tok_ok = x >= 0 && x < V;
+        if (greedy) {
+            inval = !(f_ok[j] && tok_ok);
+            stop = inval || x != f_i[j];
+        } else {
+            const float u = P.uniforms[ub + j];
+            const bool u_ok = u >= 0.f && u < 1.f;
+            inval = !(f_ok[j] && f_ok[K + 1 + j] && tok_ok && u_ok);
+            if (!inval) {
+                const float lx = load1<DT>(target_row<DT>(P, b, j), x);
+                const float dx = load1<DT>(draft_row<DT>(P, b, j), x);
+                ptok = ex2(__builtin_fmaf(lx, s, -shift_of(f_m[j], s))) / f_z[j];
+                qtok = ex2(__builtin_fmaf(dx, s, -shift_of(f_m[K + 1 + j], s))) / f_z[K + 1 + j];
+                stop = !(u * qtok < ptok);                // accept iff u*q(x) < p(x)
+            } else {
+                stop = true;
+            }
+        }
+    }
+    const uint64_t smask = __ballot(stop);
+    const uint64_t imask = __ballot(inval);
+    const int n = smask ? (__ffsll((unsigned long long)smask) - 1) : K;
+    bool bad = (n < K) && ((imask >> n) & 1ull);
+    float uK = 0.f;
+    if (!bad && n == K) bad = !f_ok[K];
+    if (!bad && !greedy) {
+        uK = P.uniforms[ub + K];
+        bad = !(uK >= 0.f && uK < 1.f);
+    }
+
+    int32_t* out = P.out + ub;
+    if (bad) {
+        if (j <= K) out[j] = -1;
+        if (j < K) {
+            put(P.p_tok, (int64_t)b * K + j, NAN);
+            put(P.q_tok, (int64_t)b * K + j, NAN);
+            put(P.lse_q, (int64_t)b * K + j, NAN);
+        }
+        if (j <= K) put(P.lse_p, ub + j, NAN);
+        if (j == 0) {
+            P.acc[b] = -1;
+            put(P.res_mass, b, NAN);
+            if (!greedy) P.rec[b].status = 0;
+        }
+        return;
+    }
+    if (j <= K) out[j] = (j < n) ? x : ((j == n && greedy) ? f_i[n] : -1);
+    const bool seen = !greedy && j <= n;
+    if (j < K) {
+        put(P.p_tok, (int64_t)b * K + j, seen ? ptok : NAN);
+        put(P.q_tok, (int64_t)b * K + j, seen ? qtok : NAN);
+        put(P.lse_q, (int64_t)b * K + j,
+            seen ? (shift_of(f_m[K + 1 + j], s) + log2f(f_z[K + 1 + j])) * LN2 : NAN);
+    }
+    if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_m[j], s) + log2f(f_z[j])) * LN2 : NAN);
+    if (j == 0) {
+        P.acc[b] = n;
+        if (greedy) {
+            put(P.res_mass, b, 0.f);
+        } else {
+            SeqRec r;
+            r.n = n;
+            r.status = 1;
+            r.mp = f_m[n];
+            r.zp = f_z[n];
+            r.mq = n < K ? f_m[K + 1 + n] : 0.f;
+            r.zq = n < K ? f_z[K + 1 + n] : 1.f;
+            r.u = uK;
+            r.pad = 0;
+            P.rec[b] = r;
+        }
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT) void k_stats(const Params P)
+{
+    const int K = P.K, R = 2 * K + 1;
+    const int per_seq = R * P.C;
+    const int b = blockIdx.x / per_seq;
+    const int rem = blockIdx.x - b * per_seq;
+    const int r = rem / P.C;
+    const int c = rem - r * P.C;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    const bool is_draft = r > K;
+    __shared__ SmState sh_sm[NWAVE];
+    __shared__ AmState sh_am[NWAVE];
+    __shared__ int sh_last;
+
+    if (!(is_draft && (greedy || P.draft == nullptr))) {
+        const char* row = is_draft ? draft_row<DT>(P, b, r - K - 1) : target_row<DT>(P, b, r);
+        constexpr int E = Fmt<DT>::E;
+        const int64_t nvec = ((int64_t)P.V + E - 1) / E;
+        const int64_t cl = ((nvec + P.C - 1) / P.C) * E;  // chunk length, a multiple of E
+        const int64_t e0 = (int64_t)c * cl;
+        const int64_t e1 = e0 + cl < (int64_t)P.V ? e0 + cl : (int64_t)P.V;
+        Partial* dst = P.part + ((int64_t)b * R + r) * P.C + c;
+        SmState sm = {NEG_INF, 0.f};
+        AmState am = {NEG_INF, INT_MAX, 0u};
+        if (greedy) {
+            if (e0 < e1) scan_chunk<DT, true>(row, e0, e1, P.s, sm, am);
+            am = block_reduce_am(am, sh_am);
+            if (threadIdx.x == 0) *dst = {am.v, 0.f, am.i, am.bad};
+        } else {
+            if (e0 < e1) scan_chunk<DT, false>(row, e0, e1, P.s, sm, am);
+            sm = block_reduce_sm(sm, P.s, sh_sm);
+            if (threadIdx.x == 0) *dst = {sm.m, sm.z, 0, 0u};
+        }
+    }
+    if (arrive_last(P.cnt1 + b, (uint32_t)per_seq, &sh_last)) finalize_seq<DT>(P, b, greedy);
+}
+
+// ----------------------------------------------------- draw: final token --
+
+// Draw weight of one element: residual max(0, p - q) scaled by Z_p, or p*Z_p.
+__device__ __forceinline__ float weight(float l, float d, float s, float cp, float cq, float w, int mode)
+{
+    const float ep = ex2(__builtin_fmaf(l, s, -cp));
+    if (mode != 0) return ep;                       // bonus row or p fallback
+    const float eq = ex2(__builtin_fmaf(d, s, -cq));
+    return fmaxf(0.f, __builtin_fmaf(-w, eq, ep));
+}
+
+template <int DT>
+__device__ void draw_search(const Params& P, int b, const SeqRec& rec, const char* trow,
+                            const char* drow, float cp, float cq, float w, bool bonus)
+{
+    constexpr int E = Fmt<DT>::E;
+    constexpr int SEG = 64 * E;
+    const int K = P.K, V = P.V, nseg = P.nseg;
+    const float s = P.s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float sh_scan[NWAVE];
+    __shared__ int sh_seg[NWAVE];
+    __shared__ float sh_lo[NWAVE];
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+
+    const float* sums_r = P.seg + (int64_t)b * nseg;
+    const float* sums_p = P.seg + ((int64_t)P.B + b) * nseg;
+
+    // total residual weight, in the same chunked scan order used for the search
+    float S = 0.f;
+    for (int base = 0; base < nseg; base += NT) {
+        const float v = (base + tid < nseg) ? sums_r[base + tid] : 0.f;
+        float tot;
+        block_incl_scan(v, sh_scan, &tot);
+        S += tot;
+    }
+    int mode = bonus ? 1 : 0;
+    const float* sums = sums_r;
+    if (!(S > 0.f)) {                              // residual rounded to nothing: draw from p_n
+        mode = 2;
+        sums = sums_p;
+        S = 0.f;
+        for (int base = 0; base < nseg; base += NT) {
+            const float v = (base + tid < nseg) ? sums[base + tid] : 0.f;
+            float tot;
+            block_incl_scan(v, sh_scan, &tot);
+            S += tot;
+        }
+    }
+    const float thr = rec.u * S;
+
+    // first segment whose running sum exceeds thr.  Only segments with
+    // positive weight can hit, so rounding in the tree prefix can never pick
+    // an empty segment.
+    int g = -1;
+    float lo = 0.f;
+    float off = 0.f;
+    for (int base = 0; base < nseg; base += NT) {
+        const float v = (base + tid < nseg) ? sums[base + tid] : 0.f;
+        float tot;
+        const float incl = block_incl_scan(v, sh_scan, &tot);
+        const bool hit = (base + tid < nseg) && v > 0.f && (off + incl > thr);
+        const uint64_t m = __ballot(hit);
+        if (lane == 0) sh_seg[wave] = m ? base + wave * 64 + (__ffsll((unsigned long long)m) - 1) : INT_MAX;
+        __syncthreads();
+        int best = INT_MAX;
+#pragma unroll
+        for (int w2 = 0; w2 < NWAVE; ++w2) best = min(best, sh_seg[w2]);
+        if (best != INT_MAX) {                    // uniform across the workgroup
+            if (base + tid == best) sh_lo[0] = off + (incl - v);
+            __syncthreads();
+            g = best;
+            lo = sh_lo[0];
+            break;
+        }
+        off += tot;
+        __syncthreads();
+    }
+    const bool overrun = g < 0;
+    if (overrun) {
+        // rounding overrun: the last segment with positive weight
+        for (int base = ((nseg - 1) / NT) * NT; base >= 0 && g < 0; base -= NT) {
+            const bool pos = (base + tid < nseg) && sums[base + tid] > 0.f;
+            const uint64_t m = __ballot(pos);
+            if (lane == 0) sh_seg[wave] = m ? base + wave * 64 + (63 - __clzll((long long)m)) : -1;
+            __syncthreads();
+            int bestl = -1;
+#pragma unroll
+            for (int w2 = 0; w2 < NWAVE; ++w2) bestl = max(bestl, sh_seg[w2]);
+            g = bestl;
+            __syncthreads();
+        }
+    }
+
+    // one segment, wave 0: lane exclusive prefix, then in-lane walk.  Only a
+    // positive weight can be chosen; a segment with positive sum always has one.
+    if (wave == 0 && g >= 0) {
+        const int64_t e = (int64_t)g * SEG + (int64_t)lane * E;
+        float xl[E], xd[E], wv[E];
+        load_elems<DT>(trow, e, V, t_al, xl);
+        if (mode == 0) load_elems<DT>(drow, e, V, d_al, xd);
+        float ls = 0.f;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            wv[k] = weight(xl[k], mode == 0 ? xd[k] : 0.f, s, cp, cq, w, mode);
+            ls += wv[k];
+        }
+        const float incl = wave_incl_scan(ls);
+        const float thr2 = thr - lo;
+        float run = incl - ls;
+        int cand = -1;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            run += wv[k];
+            if (cand < 0 && wv[k] > 0.f && run > thr2) cand = k;
+        }
+        const uint64_t m = overrun ? 0ull : __ballot(cand >= 0);
+        int y;
+        if (m) {
+            const int L = __ffsll((unsigned long long)m) - 1;
+            y = (int)((int64_t)g * SEG + (int64_t)L * E + __shfl(cand, L, 64));
+        } else {
+            int lastk = -1;
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                if (wv[k] > 0.f) lastk = k;
+            const uint64_t mp = __ballot(lastk >= 0);
+            const int L = mp ? 63 - __clzll((long long)mp) : 0;
+            const int kk = __shfl(lastk, L, 64);
+            y = (int)((int64_t)g * SEG + (int64_t)L * E + (kk < 0 ? 0 : kk));
+        }
+        if (lane == 0) {
+            P.out[(int64_t)b * (K + 1) + rec.n] = y;
+            put(P.res_mass, b, mode == 2 ? 0.f : S / rec.zp);
+        }
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT) void k_draw(const Params P)
+{
+    constexpr int E = Fmt<DT>::E;
+    constexpr int SEG = 64 * E;
+    const int b = blockIdx.x / P.tiles;
+    const int t = blockIdx.x - b * P.tiles;
+    if (P.greedy != nullptr && P.greedy[b] != 0) return;
+    const SeqRec rec = P.rec[b];
+    if (rec.status != 1) return;
+    const int K = P.K, V = P.V, nseg = P.nseg;
+    const float s = P.s;
+    const int n = rec.n;
+    const bool bonus = n == K;
+    const char* trow = target_row<DT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DT>(P, b, n);
+    const float cp = shift_of(rec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
+    const float w = bonus ? 0.f : rec.zp / rec.zq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+    __shared__ int sh_last;
+
+    float xl[SPW][E], xd[SPW][E];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int seg = t * SPT + wave * SPW + k;
+        const int64_t e = (int64_t)seg * SEG + (int64_t)lane * E;
+        load_elems<DT>(trow, e, V, t_al, xl[k]);
+        if (!bonus) load_elems<DT>(drow, e, V, d_al, xd[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int seg = t * SPT + wave * SPW + k;
+        float sr = 0.f, sp = 0.f;
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            const float ep = ex2(__builtin_fmaf(xl[k][q], s, -cp));
+            sp += ep;
+            sr += bonus ? ep : weight(xl[k][q], xd[k][q], s, cp, cq, w, 0);
+        }
+        sr = wave_sum(sr);
+        sp = wave_sum(sp);
+        if (lane == 0 && seg < nseg) {
+            P.seg[(int64_t)b * nseg + seg] = sr;
+            P.seg[((int64_t)P.B + b) * nseg + seg] = sp;
+        }
+    }
+    if (arrive_last(P.cnt2 + b, (uint32_t)P.tiles, &sh_last))
+        draw_search<DT>(P, b, rec, trow, drow, cp, cq, w, bonus);
+}
+
+// -------------------------------------------------------------- host side --
+
+struct Plan {
+    int C, nseg, tiles;
+    size_t off_cnt1, off_cnt2, off_rec, off_part, off_seg, total;
+};
+
+static int env_int(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    long x = strtol(v, &end, 10);
+    return (end && *end == '\0' && x > 0 && x < INT_MAX) ? (int)x : dflt;
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* pl)
+{
+    const int E = dtype == SV_BF16 ? Fmt<SV_BF16>::E : Fmt<SV_F32>::E;
+    const int64_t R = 2 * (int64_t)K + 1;
+    const int64_t rows = (int64_t)B * R;
+    const int64_t nvec = ((int64_t)V + E - 1) / E;
+    int64_t max_c = nvec / ((int64_t)NT * UNROLL);     // at least one full window per lane
+    if (max_c < 1) max_c = 1;
+    static const int target_items = env_int("SV_TARGET_ITEMS", 4096);
+    static const int forced_c = env_int("SV_CHUNKS", 0);
+    int64_t C = rows > 0 ? (target_items + rows - 1) / rows : 1;
+    if (forced_c > 0) C = forced_c;
+    if (C > max_c) C = max_c;
+    if (C < 1) C = 1;
+    pl->C = (int)C;
+    const int64_t seg = 64 * (int64_t)E;
+    pl->nseg = (int)(((int64_t)V + seg - 1) / seg);
+    pl->tiles = (pl->nseg + SPT - 1) / SPT;
+    if (rows * C > INT_MAX || (int64_t)B * pl->tiles > INT_MAX) return false;
+    size_t o = 0;
+    pl->off_cnt1 = o; o = align_up(o + sizeof(uint32_t) * (size_t)B, 256);
+    pl->off_cnt2 = o; o = align_up(o + sizeof(uint32_t) * (size_t)B, 256);
+    pl->off_rec = o;  o = align_up(o + sizeof(SeqRec) * (size_t)B, 256);
+    pl->off_part = o; o = align_up(o + sizeof(Partial) * (size_t)(rows * C), 256);
+    pl->off_seg = o;  o = align_up(o + sizeof(float) * 2 * (size_t)B * (size_t)pl->nseg, 256);
+    pl->total = o;
+    return true;
+}
+
+static bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static int prepare(const void* target, const void* draft, const int32_t* tokens, const float* uniforms,
+                   float T, const uint8_t* greedy, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                   int32_t* acc, int32_t* out, const sv_diag* diag, void* ws, size_t ws_bytes,
+                   Params* P, Plan* pl)
+{
+    (void)greedy;
+    if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (!(T > 0.f) || !isfinite(T)) return SV_EINVAL;
+    const double sd = 1.4426950408889634074 / (double)T;
+    const float s = (float)sd;
+    if (!isfinite(s) || !(s >= 1.17549435e-38f)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    const size_t es = dtype == SV_BF16 ? 2 : 4;
+    if (!target || !uniforms || !acc || !out) return SV_EINVAL;
+    if (K > 0 && !tokens) return SV_EINVAL;
+    if (!aligned_to(target, es) || (draft && !aligned_to(draft, es))) return SV_EINVAL;
+    if (!aligned_to(uniforms, 4) || !aligned_to(acc, 4) || !aligned_to(out, 4) ||
+        (tokens && !aligned_to(tokens, 4)))
+        return SV_EINVAL;
+    if (diag) {
+        const float* d[5] = {diag->p_tok, diag->q_tok, diag->lse_p, diag->lse_q, diag->res_mass};
+        for (const float* q : d)
+            if (q && !aligned_to(q, 4)) return SV_EINVAL;
+    }
+    if (!make_plan(B, K, V, dtype, pl)) return SV_EINVAL;
+    if (!ws || !aligned_to(ws, 16) || ws_bytes < pl->total) return SV_EWORKSPACE;
+    char* w = static_cast<char*>(ws);
+    P->target = target;
+    P->draft = K > 0 ? draft : nullptr;
+    P->tokens = tokens;
+    P->uniforms = uniforms;
+    P->greedy = greedy;
+    P->acc = acc;
+    P->out = out;
+    P->p_tok = diag ? diag->p_tok : nullptr;
+    P->q_tok = diag ? diag->q_tok : nullptr;
+    P->lse_p = diag ? diag->lse_p : nullptr;
+    P->lse_q = diag ? diag->lse_q : nullptr;
+    P->res_mass = diag ? diag->res_mass : nullptr;
+    P->cnt1 = reinterpret_cast<uint32_t*>(w + pl->off_cnt1);
+    P->cnt2 = reinterpret_cast<uint32_t*>(w + pl->off_cnt2);
+    P->rec = reinterpret_cast<SeqRec*>(w + pl->off_rec);
+    P->part = reinterpret_cast<Partial*>(w + pl->off_part);
+    P->seg = reinterpret_cast<float*>(w + pl->off_seg);
+    P->B = B;
+    P->K = K;
+    P->V = V;
+    P->C = pl->C;
+    P->nseg = pl->nseg;
+    P->tiles = pl->tiles;
+    P->s = s;
+    return 1;   // ready to launch
+}
+
+static int launch_stats(const Params& P, const Plan& pl, int32_t dtype, hipStream_t st)
+{
+    const dim3 grid((unsigned)((int64_t)P.B * (2 * P.K + 1) * pl.C));
+    if (dtype == SV_BF16) hipLaunchKernelGGL(k_stats<SV_BF16>, grid, dim3(NT), 0, st, P);
+    else hipLaunchKernelGGL(k_stats<SV_F32>, grid, dim3(NT), 0, st, P);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+}
+
+static int launch_draw(const Params& P, const Plan& pl, int32_t dtype, hipStream_t st)
+{
+    const dim3 grid((unsigned)((int64_t)P.B * pl.tiles));
+    if (dtype == SV_BF16) hipLaunchKernelGGL(k_draw<SV_BF16>, grid, dim3(NT), 0, st, P);
+    else hipLaunchKernelGGL(k_draw<SV_F32>, grid, dim3(NT), 0, st, P);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+}
+
+}  // namespace sv
+
+// ------------------------------------------------------------------ C ABI --
+
+extern "C" {
+
+size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
+{
+    if (B <= 0 || K < 0 || K > SV_MAX_K || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return 0;
+    sv::Plan pl;
+    if (!sv::make_plan(B, K, V, dtype, &pl)) return 0;
+    return pl.total;
+}
+
+#define SV_ARGS_DECL                                                                           \
+    const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,          \
+        const float *uniforms, float temperature, const uint8_t *greedy_flag, int32_t B,       \
+        int32_t K, int32_t V, int32_t dtype, int32_t *accepted_len, int32_t *out_tokens,      \
+        const sv_diag *diag, void *workspace, size_t workspace_bytes, void *stream
+
+#define SV_PREPARE                                                                             \
+    sv::Params P;                                                                              \
+    sv::Plan pl;                                                                               \
+    int rc = sv::prepare(target_logits, draft_logits, draft_tokens, uniforms, temperature,     \
+                         greedy_flag, B, K, V, dtype, accepted_len, out_tokens, diag,          \
+                         workspace, workspace_bytes, &P, &pl);                                 \
+    if (rc <= 0) return rc;                                                                    \
+    hipStream_t st = static_cast<hipStream_t>(stream)
+
+int spec_verify(SV_ARGS_DECL)
+{
+    SV_PREPARE;
+    rc = sv::launch_stats(P, pl, dtype, st);
+    if (rc != SV_OK) return rc;
+    return sv::launch_draw(P, pl, dtype, st);
+}
+
+int sv_stats(SV_ARGS_DECL)
+{
+    SV_PREPARE;
+    return sv::launch_stats(P, pl, dtype, st);
+}
+
+int sv_draw(SV_ARGS_DECL)
+{
+    SV_PREPARE;
+    return sv::launch_draw(P, pl, dtype, st);
+}
+
+const char* sv_strerror(int code)
+{
+    switch (code) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument (shape, dtype, temperature, pointer or alignment)";
+    case SV_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SV_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown error";
+    }
+}
+
+int sv_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports what include/*.h declares, and rejects bad
+arguments on the host.  No kernel is launched here: every call below fails
+its host checks before any HIP call, so these run without a GPU."""
+
+import ctypes as C
+import glob
+import math
+import os
+import re
+
+import pytest
+
+from speculative_sampling_verification_06_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"#[^\n]*", "", text)
+        for m in re.finditer(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text):
+            if m.group(1) not in ("sizeof",):
+                names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert set(_declared_functions()) == set(binding.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert lib.sv_version() == 1
+    for code in (0, -1, -2, -3, 17):
+        assert isinstance(binding.strerror(code), str) and binding.strerror(code)
+
+
+def test_workspace_bytes(lib):
+    assert binding.workspace_bytes(0, 4, 32, 0) == 0
+    assert binding.workspace_bytes(4, -1, 32, 0) == 0
+    assert binding.workspace_bytes(4, 64, 32, 0) == 0
+    assert binding.workspace_bytes(4, 4, 0, 0) == 0
+    assert binding.workspace_bytes(4, 4, 32, 7) == 0
+    a = binding.workspace_bytes(256, 8, 152064, binding.SV_BF16)
+    b = binding.workspace_bytes(512, 8, 152064, binding.SV_BF16)
+    assert 0 < a < b and a % 256 == 0
+    assert binding.workspace_bytes(1, 63, 1, binding.SV_F32) > 0
+
+
+FAKE = 0x10000          # never dereferenced: every call below fails a host check
+
+
+def _call(lib, fn="spec_verify", *, target=FAKE, draft=FAKE, tokens=FAKE, uniforms=FAKE, T=1.0,
+          greedy=None, B=2, K=3, V=100, dtype=0, acc=FAKE, out=FAKE, diag=None,
+          ws=FAKE, ws_bytes=0, stream=None):
+    return getattr(lib, fn)(target, draft, tokens, uniforms, C.c_float(T), greedy, B, K, V, dtype,
+                            acc, out, diag, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("fn", ["spec_verify", "sv_stats", "sv_draw"])
+@pytest.mark.parametrize("kw", [
+    dict(K=-1), dict(K=64), dict(V=0), dict(B=-1), dict(dtype=2),
+    dict(T=0.0), dict(T=-1.0), dict(T=math.nan), dict(T=math.inf), dict(T=1e-45),
+    dict(target=None), dict(uniforms=None), dict(acc=None), dict(out=None), dict(tokens=None),
+    dict(target=FAKE + 2), dict(target=FAKE + 1, dtype=1), dict(draft=FAKE + 2), dict(tokens=FAKE + 2),
+    dict(uniforms=FAKE + 1), dict(out=FAKE + 2), dict(acc=FAKE + 3),
+])
+def test_host_rejects_bad_arguments(lib, fn, kw):
+    assert _call(lib, fn, **kw) == binding.SV_EINVAL
+
+
+def test_host_rejects_misaligned_diag(lib):
+    d = binding.SvDiag(FAKE + 2, None, None, None, None)
+    assert _call(lib, diag=C.byref(d)) == binding.SV_EINVAL
+
+
+def test_workspace_errors(lib):
+    need = binding.workspace_bytes(2, 3, 100, 0)
+    assert _call(lib, ws=None, ws_bytes=need) == binding.SV_EWORKSPACE
+    assert _call(lib, ws=FAKE + 8, ws_bytes=need) == binding.SV_EWORKSPACE
+    assert _call(lib, ws_bytes=need - 1) == binding.SV_EWORKSPACE
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _call(lib, B=0, target=None, draft=None, tokens=None, uniforms=None,
+                 acc=None, out=None, ws=None) == binding.SV_OK
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library(str(tmp_path / "nope.so"))
