@@ -8,7 +8,7 @@ B=256 sequences, K=8 draft tokens, V=152064 vocabulary, bf16 logits,
 T=1, sampling (target ~ N(0,4) + log-Zipf bias, draft = target + N(0,2.5)).
 
 Prints one JSON line: verified logits/s (B*(K+1)*V per second), the roofline
-of the dominant kernel (k_stats: HBM-bound; algorithmic bytes = every target
+of the dominant kernel (k_rowstats: HBM-bound; algorithmic bytes = every target
 row and every draft row of sampling sequences read once, V*s bytes per row,
 divided by its average duration from HIP events recorded around it on the
 launch stream), and the fp64 oracle's throughput on this host as a CPU
@@ -40,9 +40,9 @@ def _source_sha() -> str:
 
 
 def _traffic(workload_name: str):
-    """HBM bytes per k_stats launch from the committed PMC summary, if it was
+    """HBM bytes per k_rowstats launch from the committed PMC summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"k_stats_{workload_name}_traffic.txt")
+    path = os.path.join(PROFILES, f"k_rowstats_{workload_name}_traffic.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -92,7 +92,8 @@ def main() -> int:
 
     d = binding.to_device(w, dev)
     a = (d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], d["greedy"])
-    out = binding.verify(*a)                       # allocates outputs and the workspace once
+    call = binding.Bound(*a)                       # checks, outputs and workspace, once
+    out = call.verify()
     stream = torch.cuda.current_stream(dev)
 
     if args.copy_calibration_mib > 0:
@@ -105,8 +106,8 @@ def main() -> int:
         del src, dst
 
     for _ in range(args.warmup):
-        binding.stats(*a, outputs=out)
-        binding.draw(*a, outputs=out)
+        call.stats()
+        call.draw()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -115,9 +116,9 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(K):
         evs[i][0].record(stream)
-        binding.stats(*a, outputs=out)
+        call.stats()
         evs[i][1].record(stream)
-        binding.draw(*a, outputs=out)
+        call.draw()
         evs[i][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -153,13 +154,13 @@ def main() -> int:
                    "verified_logits_per_step": w.verified_logits},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": _traffic(w.name),
-                     "kernel": "k_stats", "algorithmic_bytes_per_launch": eager,
+                     "kernel": "k_rowstats", "algorithmic_bytes_per_launch": eager,
                      "avg_launch_ms": float(stats_ms.mean())},
         "timing_ms": {"step_events_median": float(np.median(step_ev_ms)),
                       "step_events_p10": float(np.percentile(step_ev_ms, 10)),
                       "step_events_p90": float(np.percentile(step_ev_ms, 90)),
-                      "k_stats_median": float(np.median(stats_ms)),
-                      "k_draw_median": float(np.median(draw_ms))},
+                      "k_rowstats_median": float(np.median(stats_ms)),
+                      "decide_search_median": float(np.median(draw_ms))},
         "method": {"accepted_len_hist": np.bincount(acc[acc >= 0], minlength=w.K + 1).tolist(),
                    "mean_accepted": float(acc[acc >= 0].mean()) if (acc >= 0).any() else None,
                    "needed_bytes": needed, "eager_bytes": eager,

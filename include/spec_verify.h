@@ -92,8 +92,8 @@ typedef struct sv_diag {
 } sv_diag;
 
 /* Bytes of device workspace spec_verify needs for this shape (0 for B == 0).
- * The workspace must be zero-filled once when allocated; every completed
- * call leaves its counters at zero again, so it can be reused as is.         */
+ * No initialisation is needed; calls sharing one workspace must be ordered
+ * on one stream.                                                            */
 size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype);
 
 /* The whole verify step (steps: row statistics, acceptance tests, first
@@ -116,11 +116,12 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* The same call split in its two launches, for timing and for checking the
- * split against the whole: sv_stats streams every row once and settles n,
- * the accepted prefix and greedy results; sv_draw makes the final draw of
- * sampling sequences.  sv_draw must follow sv_stats on the same stream with
- * identical arguments.                                                       */
+/* The same call in two parts, for timing and for checking the parts against
+ * the whole: sv_stats streams every target row, and the draft rows of
+ * sampling sequences, once into per-chunk
+ * statistics (the HBM-bound part); sv_draw settles n, writes the outputs and
+ * makes the final draw of sampling sequences.  sv_draw must follow sv_stats
+ * on the same stream with identical arguments.                              */
 int sv_stats(const void* target_logits, const void* draft_logits,
              const int32_t* draft_tokens, const float* uniforms,
              float temperature, const uint8_t* greedy_flag,

@@ -85,10 +85,9 @@ _ws_cache: dict = {}
 
 
 def get_workspace(nbytes: int, device):
-    """A zero-filled workspace of at least nbytes on `device`, reused across calls.
+    """A workspace of at least nbytes on `device`, reused across calls.
 
-    The kernels leave its counters at zero after every completed call, so it
-    is zeroed once, when allocated.
+    Calls that share it are ordered on the caller's stream.
     """
     torch = _torch()
     key = (str(device),)
@@ -212,3 +211,59 @@ def to_device(w, device="cuda:0"):
         uniforms=torch.from_numpy(np.ascontiguousarray(w.uniforms, np.float32)).to(device),
         greedy=torch.from_numpy(np.ascontiguousarray(w.greedy, np.uint8)).to(device),
         temperature=float(w.T))
+
+
+class Bound:
+    """One verify problem bound to fixed device tensors: the C arguments are
+    marshalled once, so each call is a single ctypes call (a few microseconds
+    of host time) and back-to-back launches keep the GPU busy.
+
+    Checks happen in the constructor (the same checks as verify()); the
+    tensors must stay alive and keep their shapes while the object is used.
+    """
+
+    def __init__(self, target, draft, tokens, uniforms, temperature, greedy=None, *,
+                 outputs=None, diag=True, stream=None):
+        torch = _torch()
+        # one checked call builds the outputs and the workspace
+        self.outputs = _call("sv_stats", target, draft, tokens, uniforms, temperature, greedy,
+                             outputs=outputs, diag=diag, stream=stream)
+        torch.cuda.synchronize(target.device)
+        lib = load_library()
+        B, K1, V = target.shape
+        K = K1 - 1
+        dt = _dtype_code(target)
+        o = self.outputs
+        self._dg = None
+        if "p_tok" in o:
+            self._dg = SvDiag(*[_dev_ptr(o[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
+        ws = get_workspace(lib.sv_workspace_bytes(B, K, V, dt), target.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(target.device).cuda_stream
+        self._keep = (target, draft, tokens, uniforms, greedy, ws)
+        self._args = (
+            C.c_void_p(target.data_ptr()), C.c_void_p(None if draft is None else draft.data_ptr()),
+            C.c_void_p(None if tokens is None or tokens.numel() == 0 else tokens.data_ptr()),
+            C.c_void_p(uniforms.data_ptr()), C.c_float(float(temperature)),
+            C.c_void_p(None if greedy is None else greedy.data_ptr()),
+            C.c_int32(B), C.c_int32(K), C.c_int32(V), C.c_int32(dt),
+            C.c_void_p(o["accepted_len"].data_ptr()), C.c_void_p(o["out_tokens"].data_ptr()),
+            None if self._dg is None else C.byref(self._dg),
+            C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel()), C.c_void_p(stream))
+        self._verify, self._stats, self._draw = lib.spec_verify, lib.sv_stats, lib.sv_draw
+
+    def _check(self, rc):
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, strerror(rc))
+
+    def verify(self):
+        self._check(self._verify(*self._args))
+        return self.outputs
+
+    def stats(self):
+        self._check(self._stats(*self._args))
+        return self.outputs
+
+    def draw(self):
+        self._check(self._draw(*self._args))
+        return self.outputs

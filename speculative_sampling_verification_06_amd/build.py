@@ -19,10 +19,12 @@ SOURCES = ["spec_verify.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: hipcc must not emit v_pk_{add,mul,fma}_f32.
+# No fp contraction: every fma the kernels want is written out, and a rescale
+# exp2(c_old - c_new) must use the rounded shifts the terms were computed with.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-fno-fast-math", "-Wall", "-Wno-unused-function",
+    "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
 ]
 
 

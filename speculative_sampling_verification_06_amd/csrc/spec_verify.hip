@@ -2,31 +2,34 @@
 // verify step.  Page citations ([QH], [NL], [MC]) are spelled out in
 // include/spec_verify.h next to the declarations.
 //
-// Two launches, both HBM streams:
+// Three launches on the caller's stream; kernel boundaries are the only
+// synchronisation between workgroups (no fences, no counters):
 //
-//   k_stats  one workgroup per (sequence b, row r, vocab chunk c).  Rows
-//            r = 0..K are target rows, r = K+1..2K draft rows.  The chunk is
-//            streamed once with 16-byte loads (UNROLL of them in flight per
-//            lane); sampling rows keep an online softmax state (running max m
-//            and sum z of exp2(x*s - m*s), s = log2(e)/T), greedy rows keep a
-//            lowest-index argmax.  The partial goes to the workspace; the last
-//            workgroup of the sequence to arrive (self-resetting atomic
-//            counter) merges the partials in a fixed order, evaluates the K
-//            acceptance tests on wave 0, finds the first rejection with one
-//            64-lane ballot, writes the accepted prefix and the greedy result
-//            and records what the draw needs.
-//   k_draw   one workgroup per (sampling sequence b, tile of row n).  Each
-//            wave sums the draw weights (residual max(0, p - q) scaled by Z_p,
-//            or p for the bonus) over 64*E-element segments; the last tile to
-//            arrive scans the segment sums, re-reads the one segment that
-//            holds u*S, scans it lane by lane and writes the final token.
+//   k_rowstats  one workgroup per (sequence b, row r, vocab chunk c).  Rows
+//               r = 0..K are target rows, r = K+1..2K draft rows.  The chunk
+//               is streamed once with 16-byte loads (UNROLL in flight per
+//               lane); sampling rows keep an online softmax state (running max
+//               m and sum z of exp2(x*s - m*s), s = log2(e)/T), greedy rows a
+//               lowest-index argmax.  One 16-byte partial per chunk goes to
+//               the workspace.  This is the HBM stream: every logit once.
+//   k_decide    one workgroup per (sequence b, vocab tile t).  Each merges the
+//               sequence's partials in chunk order, runs the K acceptance tests
+//               on wave 0 and finds the first rejection n with one ballot;
+//               tile 0 writes accepted_len, the accepted prefix, the greedy
+//               token and the diagnostics.  Sampling sequences then sum the
+//               draw weights of row n (residual max(0, p - q) scaled by Z_p, or
+//               p for the bonus) per 64*E-element segment of the tile.
+//   k_search    one workgroup per sampling sequence: scans the segment sums
+//               for u*S, re-reads that one segment and walks it lane by lane.
 //
 // Numerics: every term is exp2(fma(x, s, -c)) with c = m*s held as an exact
 // shift, so the row's own rounding of c cancels out of every ratio; partial
-// states are merged by rescaling with exp2(c_i - c).  Sums are fp32 trees
-// (window, wave butterfly, fixed-order merges), never float atomics, so the
-// result is bitwise deterministic.  The max is NaN-propagating, so a NaN
-// anywhere in a row turns its sum into NaN and the row is reported invalid.
+// states are merged by rescaling with exp2(c_i - c), c_i the rounded shifts
+// the terms were computed with (built with -ffp-contract=off so this stays
+// exact).  Sums are fp32 trees (window, wave butterfly, fixed-order merges),
+// never float atomics, so results are bitwise deterministic.  The max is
+// NaN-propagating, so a NaN anywhere in a row turns its sum into NaN and the
+// row is reported invalid.
 
 #include <hip/hip_runtime.h>
 
@@ -67,7 +70,7 @@ struct Partial {      // one (row, chunk): softmax {m, z} or argmax {m = value, 
     uint32_t bad;
 };
 
-struct SeqRec {       // what k_stats leaves for k_draw
+struct SeqRec {       // what k_decide (tile 0) leaves for k_search
     int32_t n;
     int32_t status;   // 1 = sampling sequence, valid, draw pending
     float mp, zp;     // target row n
@@ -91,8 +94,6 @@ struct Params {
     float* res_mass;
     Partial* part;
     SeqRec* rec;
-    uint32_t* cnt1;
-    uint32_t* cnt2;
     float* seg;       // [2][B][nseg]: residual sums, then p sums
     int32_t B, K, V, C;
     int32_t nseg, tiles;
@@ -352,22 +353,6 @@ __device__ __forceinline__ float block_incl_scan(float v, float* sh, float* tota
     return v + off;
 }
 
-// Arrival on a per-sequence counter that wraps back to zero after `total`
-// arrivals.  Returns true in the last workgroup to arrive, after an acquire.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, int* sh_flag)
-{
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();                                   // release this group's writes
-        const uint32_t old = atomicInc(counter, total - 1u);
-        *sh_flag = (old == total - 1u);
-    }
-    __syncthreads();
-    const bool last = *sh_flag != 0;
-    if (last) __threadfence();                             // acquire everyone else's
-    return last;
-}
-
 template <int DT>
 __device__ __forceinline__ const char* target_row(const Params& P, int b, int j)
 {
@@ -383,10 +368,59 @@ __device__ __forceinline__ const char* draft_row(const Params& P, int b, int j)
 
 __device__ __forceinline__ void put(float* a, int64_t i, float v) { if (a) a[i] = v; }
 
-// ---------------------------------------------- stats: settle n per sequence --
+// --------------------------------------------- k_rowstats: one row chunk --
 
 template <int DT>
-__device__ void finalize_seq(const Params& P, int b, bool greedy)
+__global__ __launch_bounds__(NT) void k_rowstats(const Params P)
+{
+    const int K = P.K, R = 2 * K + 1;
+    const int per_seq = R * P.C;
+    const int b = blockIdx.x / per_seq;
+    const int rem = blockIdx.x - b * per_seq;
+    const int r = rem / P.C;
+    const int c = rem - r * P.C;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    const bool is_draft = r > K;
+    __shared__ SmState sh_sm[NWAVE];
+    __shared__ AmState sh_am[NWAVE];
+
+    if (is_draft && (greedy || P.draft == nullptr)) return;      // never read
+    const char* row = is_draft ? draft_row<DT>(P, b, r - K - 1) : target_row<DT>(P, b, r);
+    constexpr int E = Fmt<DT>::E;
+    const int64_t nvec = ((int64_t)P.V + E - 1) / E;
+    const int64_t cl = ((nvec + P.C - 1) / P.C) * E;              // chunk length, a multiple of E
+    const int64_t e0 = (int64_t)c * cl;
+    const int64_t e1 = e0 + cl < (int64_t)P.V ? e0 + cl : (int64_t)P.V;
+    Partial* dst = P.part + ((int64_t)b * R + r) * P.C + c;
+    SmState sm = {NEG_INF, 0.f};
+    AmState am = {NEG_INF, INT_MAX, 0u};
+    if (greedy) {
+        if (e0 < e1) scan_chunk<DT, true>(row, e0, e1, P.s, sm, am);
+        am = block_reduce_am(am, sh_am);
+        if (threadIdx.x == 0) *dst = {am.v, 0.f, am.i, am.bad};
+    } else {
+        if (e0 < e1) scan_chunk<DT, false>(row, e0, e1, P.s, sm, am);
+        sm = block_reduce_sm(sm, P.s, sh_sm);
+        if (threadIdx.x == 0) *dst = {sm.m, sm.z, 0, 0u};
+    }
+}
+
+// ------------------------------------------ decide: n for one sequence --
+
+struct Decision {
+    int32_t n;
+    int32_t ok;       // valid sequence
+    float mp, zp, mq, zq, u;
+};
+
+// Merge the sequence's chunk partials (fixed chunk order), run the K tests on
+// wave 0 and find the first rejection with one ballot.  Called by every
+// workgroup that needs n; all of them reach the same result bit for bit.  With
+// write_out, also writes accepted_len, the accepted prefix, the greedy token,
+// the diagnostics and the record the search launch reads.  Every thread of the
+// workgroup must call it; *dec is valid for all threads on return.
+template <int DT>
+__device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, Decision* dec)
 {
     const int K = P.K, V = P.V, C = P.C, R = 2 * K + 1;
     const float s = P.s;
@@ -395,7 +429,6 @@ __device__ void finalize_seq(const Params& P, int b, bool greedy)
     __shared__ int32_t f_i[MAXR];
     __shared__ int32_t f_ok[MAXR];
 
-    // merge the C chunk partials of every row, in chunk order
     if (tid < R) {
         const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
         if (greedy) {
@@ -419,125 +452,97 @@ __device__ void finalize_seq(const Params& P, int b, bool greedy)
         }
     }
     __syncthreads();
-    if (tid >= 64) return;                              // wave 0 decides; no barrier below
 
-    const int j = tid;
-    const int64_t ub = (int64_t)b * (K + 1);
-    bool stop = false, inval = false;
-    float ptok = NAN, qtok = NAN;
-    int32_t x = -1;
-    if (j < K) {
-        x = P.tokens[(int64_t)b * K + j];
-        const bool tok_ok = x >= 0 && x < V;
-        if (greedy) {
-            inval = !(f_ok[j] && tok_ok);
-            stop = inval || x != f_i[j];
-        } else {
-            const float u = P.uniforms[ub + j];
-            const bool u_ok = u >= 0.f && u < 1.f;
-            inval = !(f_ok[j] && f_ok[K + 1 + j] && tok_ok && u_ok);
-            if (!inval) {
-                const float lx = load1<DT>(target_row<DT>(P, b, j), x);
-                const float dx = load1<DT>(draft_row<DT>(P, b, j), x);
-                ptok = ex2(__builtin_fmaf(lx, s, -shift_of(f_m[j], s))) / f_z[j];
-                qtok = ex2(__builtin_fmaf(dx, s, -shift_of(f_m[K + 1 + j], s))) / f_z[K + 1 + j];
-                stop = !(u * qtok < ptok);                // accept iff u*q(x) < p(x)
+    if (tid < 64) {
+        const int j = tid;
+        const int64_t ub = (int64_t)b * (K + 1);
+        bool stop = false, inval = false;
+        float ptok = NAN, qtok = NAN;
+        int32_t x = -1;
+        if (j < K) {
+            x = P.tokens[(int64_t)b * K + j];
+            const bool tok_ok = x >= 0 && x < V;
+            if (greedy) {
+                inval = !(f_ok[j] && tok_ok);
+                stop = inval || x != f_i[j];
             } else {
-                stop = true;
+                const float u = P.uniforms[ub + j];
+                const bool u_ok = u >= 0.f && u < 1.f;
+                inval = !(f_ok[j] && f_ok[K + 1 + j] && tok_ok && u_ok);
+                if (!inval) {
+                    const float lx = load1<DT>(target_row<DT>(P, b, j), x);
+                    const float dx = load1<DT>(draft_row<DT>(P, b, j), x);
+                    ptok = ex2(__builtin_fmaf(lx, s, -shift_of(f_m[j], s))) / f_z[j];
+                    qtok = ex2(__builtin_fmaf(dx, s, -shift_of(f_m[K + 1 + j], s))) / f_z[K + 1 + j];
+                    stop = !(u * qtok < ptok);            // accept iff u*q(x) < p(x)
+                } else {
+                    stop = true;
+                }
+            }
+        }
+        const uint64_t smask = __ballot(stop);
+        const uint64_t imask = __ballot(inval);
+        const int n = smask ? (__ffsll((unsigned long long)smask) - 1) : K;
+        bool bad = (n < K) && ((imask >> n) & 1ull);
+        float uK = 0.f;
+        if (!bad && n == K) bad = !f_ok[K];
+        if (!bad && !greedy) {
+            uK = P.uniforms[ub + K];
+            bad = !(uK >= 0.f && uK < 1.f);
+        }
+        if (j == 0) {
+            dec->n = n;
+            dec->ok = !bad;
+            dec->mp = bad || greedy ? 0.f : f_m[n];
+            dec->zp = bad || greedy ? 1.f : f_z[n];
+            dec->mq = (bad || greedy || n == K) ? 0.f : f_m[K + 1 + n];
+            dec->zq = (bad || greedy || n == K) ? 1.f : f_z[K + 1 + n];
+            dec->u = uK;
+        }
+        if (write_out) {
+            int32_t* out = P.out + ub;
+            if (bad) {
+                if (j <= K) out[j] = -1;
+                if (j < K) {
+                    put(P.p_tok, (int64_t)b * K + j, NAN);
+                    put(P.q_tok, (int64_t)b * K + j, NAN);
+                    put(P.lse_q, (int64_t)b * K + j, NAN);
+                }
+                if (j <= K) put(P.lse_p, ub + j, NAN);
+                if (j == 0) {
+                    P.acc[b] = -1;
+                    put(P.res_mass, b, NAN);
+                }
+            } else {
+                if (j <= K) out[j] = (j < n) ? x : ((j == n && greedy) ? f_i[n] : -1);
+                const bool seen = !greedy && j <= n;
+                if (j < K) {
+                    put(P.p_tok, (int64_t)b * K + j, seen ? ptok : NAN);
+                    put(P.q_tok, (int64_t)b * K + j, seen ? qtok : NAN);
+                    put(P.lse_q, (int64_t)b * K + j,
+                        seen ? (shift_of(f_m[K + 1 + j], s) + log2f(f_z[K + 1 + j])) * LN2 : NAN);
+                }
+                if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_m[j], s) + log2f(f_z[j])) * LN2 : NAN);
+                if (j == 0) {
+                    P.acc[b] = n;
+                    if (greedy) put(P.res_mass, b, 0.f);
+                }
+            }
+            if (j == 0) {
+                SeqRec r;
+                r.n = n;
+                r.status = (!bad && !greedy) ? 1 : 0;
+                r.mp = f_m[n];
+                r.zp = greedy ? 1.f : f_z[n];
+                r.mq = (greedy || n == K) ? 0.f : f_m[K + 1 + n];
+                r.zq = (greedy || n == K) ? 1.f : f_z[K + 1 + n];
+                r.u = uK;
+                r.pad = 0;
+                P.rec[b] = r;
             }
         }
     }
-    const uint64_t smask = __ballot(stop);
-    const uint64_t imask = __ballot(inval);
-    const int n = smask ? (__ffsll((unsigned long long)smask) - 1) : K;
-    bool bad = (n < K) && ((imask >> n) & 1ull);
-    float uK = 0.f;
-    if (!bad && n == K) bad = !f_ok[K];
-    if (!bad && !greedy) {
-        uK = P.uniforms[ub + K];
-        bad = !(uK >= 0.f && uK < 1.f);
-    }
-
-    int32_t* out = P.out + ub;
-    if (bad) {
-        if (j <= K) out[j] = -1;
-        if (j < K) {
-            put(P.p_tok, (int64_t)b * K + j, NAN);
-            put(P.q_tok, (int64_t)b * K + j, NAN);
-            put(P.lse_q, (int64_t)b * K + j, NAN);
-        }
-        if (j <= K) put(P.lse_p, ub + j, NAN);
-        if (j == 0) {
-            P.acc[b] = -1;
-            put(P.res_mass, b, NAN);
-            if (!greedy) P.rec[b].status = 0;
-        }
-        return;
-    }
-    if (j <= K) out[j] = (j < n) ? x : ((j == n && greedy) ? f_i[n] : -1);
-    const bool seen = !greedy && j <= n;
-    if (j < K) {
-        put(P.p_tok, (int64_t)b * K + j, seen ? ptok : NAN);
-        put(P.q_tok, (int64_t)b * K + j, seen ? qtok : NAN);
-        put(P.lse_q, (int64_t)b * K + j,
-            seen ? (shift_of(f_m[K + 1 + j], s) + log2f(f_z[K + 1 + j])) * LN2 : NAN);
-    }
-    if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_m[j], s) + log2f(f_z[j])) * LN2 : NAN);
-    if (j == 0) {
-        P.acc[b] = n;
-        if (greedy) {
-            put(P.res_mass, b, 0.f);
-        } else {
-            SeqRec r;
-            r.n = n;
-            r.status = 1;
-            r.mp = f_m[n];
-            r.zp = f_z[n];
-            r.mq = n < K ? f_m[K + 1 + n] : 0.f;
-            r.zq = n < K ? f_z[K + 1 + n] : 1.f;
-            r.u = uK;
-            r.pad = 0;
-            P.rec[b] = r;
-        }
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(NT) void k_stats(const Params P)
-{
-    const int K = P.K, R = 2 * K + 1;
-    const int per_seq = R * P.C;
-    const int b = blockIdx.x / per_seq;
-    const int rem = blockIdx.x - b * per_seq;
-    const int r = rem / P.C;
-    const int c = rem - r * P.C;
-    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
-    const bool is_draft = r > K;
-    __shared__ SmState sh_sm[NWAVE];
-    __shared__ AmState sh_am[NWAVE];
-    __shared__ int sh_last;
-
-    if (!(is_draft && (greedy || P.draft == nullptr))) {
-        const char* row = is_draft ? draft_row<DT>(P, b, r - K - 1) : target_row<DT>(P, b, r);
-        constexpr int E = Fmt<DT>::E;
-        const int64_t nvec = ((int64_t)P.V + E - 1) / E;
-        const int64_t cl = ((nvec + P.C - 1) / P.C) * E;  // chunk length, a multiple of E
-        const int64_t e0 = (int64_t)c * cl;
-        const int64_t e1 = e0 + cl < (int64_t)P.V ? e0 + cl : (int64_t)P.V;
-        Partial* dst = P.part + ((int64_t)b * R + r) * P.C + c;
-        SmState sm = {NEG_INF, 0.f};
-        AmState am = {NEG_INF, INT_MAX, 0u};
-        if (greedy) {
-            if (e0 < e1) scan_chunk<DT, true>(row, e0, e1, P.s, sm, am);
-            am = block_reduce_am(am, sh_am);
-            if (threadIdx.x == 0) *dst = {am.v, 0.f, am.i, am.bad};
-        } else {
-            if (e0 < e1) scan_chunk<DT, false>(row, e0, e1, P.s, sm, am);
-            sm = block_reduce_sm(sm, P.s, sh_sm);
-            if (threadIdx.x == 0) *dst = {sm.m, sm.z, 0, 0u};
-        }
-    }
-    if (arrive_last(P.cnt1 + b, (uint32_t)per_seq, &sh_last)) finalize_seq<DT>(P, b, greedy);
+    __syncthreads();
 }
 
 // ----------------------------------------------------- draw: final token --
@@ -551,14 +556,82 @@ __device__ __forceinline__ float weight(float l, float d, float s, float cp, flo
     return fmaxf(0.f, __builtin_fmaf(-w, eq, ep));
 }
 
+// k_decide: one workgroup per (sequence b, tile t of the vocabulary).  Every
+// workgroup settles n itself (tile 0 also writes the outputs); sampling
+// sequences then sum the draw weights of row n over the tile's segments
+// (64*E elements, one per wave iteration) into the workspace.
 template <int DT>
-__device__ void draw_search(const Params& P, int b, const SeqRec& rec, const char* trow,
-                            const char* drow, float cp, float cq, float w, bool bonus)
+__global__ __launch_bounds__(NT) void k_decide(const Params P)
 {
     constexpr int E = Fmt<DT>::E;
     constexpr int SEG = 64 * E;
+    const int b = blockIdx.x / P.tiles;
+    const int t = blockIdx.x - b * P.tiles;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    if (greedy && t > 0) return;
+    __shared__ Decision dec;
+    decide_seq<DT>(P, b, greedy, t == 0, &dec);
+    if (greedy || !dec.ok) return;                  // uniform: dec is shared
+
     const int K = P.K, V = P.V, nseg = P.nseg;
     const float s = P.s;
+    const int n = dec.n;
+    const bool bonus = n == K;
+    const char* trow = target_row<DT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DT>(P, b, n);
+    const float cp = shift_of(dec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(dec.mq, s);
+    const float w = bonus ? 0.f : dec.zp / dec.zq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+
+    float xl[SPW][E], xd[SPW][E];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int seg = t * SPT + wave * SPW + k;
+        const int64_t e = (int64_t)seg * SEG + (int64_t)lane * E;
+        load_elems<DT>(trow, e, V, t_al, xl[k]);
+        if (!bonus) load_elems<DT>(drow, e, V, d_al, xd[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int seg = t * SPT + wave * SPW + k;
+        float sr = 0.f, sp = 0.f;
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            const float ep = ex2(__builtin_fmaf(xl[k][q], s, -cp));
+            sp += ep;
+            sr += bonus ? ep : weight(xl[k][q], xd[k][q], s, cp, cq, w, 0);
+        }
+        sr = wave_sum(sr);
+        sp = wave_sum(sp);
+        if (lane == 0 && seg < nseg) {
+            P.seg[(int64_t)b * nseg + seg] = sr;
+            P.seg[((int64_t)P.B + b) * nseg + seg] = sp;
+        }
+    }
+}
+
+// k_search: one workgroup per sequence.  Scans the segment sums for the one
+// segment holding u*S, then walks that segment lane by lane.
+template <int DT>
+__global__ __launch_bounds__(NT) void k_search(const Params P)
+{
+    constexpr int E = Fmt<DT>::E;
+    constexpr int SEG = 64 * E;
+    const int b = blockIdx.x;
+    const SeqRec rec = P.rec[b];
+    if (rec.status != 1) return;
+    const int K = P.K, V = P.V, nseg = P.nseg;
+    const float s = P.s;
+    const int n = rec.n;
+    const bool bonus = n == K;
+    const char* trow = target_row<DT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DT>(P, b, n);
+    const float cp = shift_of(rec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
+    const float w = bonus ? 0.f : rec.zp / rec.zq;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float sh_scan[NWAVE];
     __shared__ int sh_seg[NWAVE];
@@ -569,7 +642,7 @@ __device__ void draw_search(const Params& P, int b, const SeqRec& rec, const cha
     const float* sums_r = P.seg + (int64_t)b * nseg;
     const float* sums_p = P.seg + ((int64_t)P.B + b) * nseg;
 
-    // total residual weight, in the same chunked scan order used for the search
+    // total weight, in the chunked scan order the search uses
     float S = 0.f;
     for (int base = 0; base < nseg; base += NT) {
         const float v = (base + tid < nseg) ? sums_r[base + tid] : 0.f;
@@ -593,8 +666,8 @@ __device__ void draw_search(const Params& P, int b, const SeqRec& rec, const cha
     const float thr = rec.u * S;
 
     // first segment whose running sum exceeds thr.  Only segments with
-    // positive weight can hit, so rounding in the tree prefix can never pick
-    // an empty segment.
+    // positive weight can hit, so rounding in the tree prefix never picks an
+    // empty one.
     int g = -1;
     float lo = 0.f;
     float off = 0.f;
@@ -635,8 +708,9 @@ __device__ void draw_search(const Params& P, int b, const SeqRec& rec, const cha
         }
     }
 
-    // one segment, wave 0: lane exclusive prefix, then in-lane walk.  Only a
-    // positive weight can be chosen; a segment with positive sum always has one.
+    // one segment on wave 0: lane exclusive prefix, then an in-lane walk.
+    // Only a positive weight can be chosen; a segment with a positive sum
+    // always holds one.
     if (wave == 0 && g >= 0) {
         const int64_t e = (int64_t)g * SEG + (int64_t)lane * E;
         float xl[E], xd[E], wv[E];
@@ -673,70 +747,17 @@ __device__ void draw_search(const Params& P, int b, const SeqRec& rec, const cha
             y = (int)((int64_t)g * SEG + (int64_t)L * E + (kk < 0 ? 0 : kk));
         }
         if (lane == 0) {
-            P.out[(int64_t)b * (K + 1) + rec.n] = y;
+            P.out[(int64_t)b * (K + 1) + n] = y;
             put(P.res_mass, b, mode == 2 ? 0.f : S / rec.zp);
         }
     }
-}
-
-template <int DT>
-__global__ __launch_bounds__(NT) void k_draw(const Params P)
-{
-    constexpr int E = Fmt<DT>::E;
-    constexpr int SEG = 64 * E;
-    const int b = blockIdx.x / P.tiles;
-    const int t = blockIdx.x - b * P.tiles;
-    if (P.greedy != nullptr && P.greedy[b] != 0) return;
-    const SeqRec rec = P.rec[b];
-    if (rec.status != 1) return;
-    const int K = P.K, V = P.V, nseg = P.nseg;
-    const float s = P.s;
-    const int n = rec.n;
-    const bool bonus = n == K;
-    const char* trow = target_row<DT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DT>(P, b, n);
-    const float cp = shift_of(rec.mp, s);
-    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
-    const float w = bonus ? 0.f : rec.zp / rec.zq;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
-    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
-    __shared__ int sh_last;
-
-    float xl[SPW][E], xd[SPW][E];
-#pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-        const int seg = t * SPT + wave * SPW + k;
-        const int64_t e = (int64_t)seg * SEG + (int64_t)lane * E;
-        load_elems<DT>(trow, e, V, t_al, xl[k]);
-        if (!bonus) load_elems<DT>(drow, e, V, d_al, xd[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-        const int seg = t * SPT + wave * SPW + k;
-        float sr = 0.f, sp = 0.f;
-#pragma unroll
-        for (int q = 0; q < E; ++q) {
-            const float ep = ex2(__builtin_fmaf(xl[k][q], s, -cp));
-            sp += ep;
-            sr += bonus ? ep : weight(xl[k][q], xd[k][q], s, cp, cq, w, 0);
-        }
-        sr = wave_sum(sr);
-        sp = wave_sum(sp);
-        if (lane == 0 && seg < nseg) {
-            P.seg[(int64_t)b * nseg + seg] = sr;
-            P.seg[((int64_t)P.B + b) * nseg + seg] = sp;
-        }
-    }
-    if (arrive_last(P.cnt2 + b, (uint32_t)P.tiles, &sh_last))
-        draw_search<DT>(P, b, rec, trow, drow, cp, cq, w, bonus);
 }
 
 // -------------------------------------------------------------- host side --
 
 struct Plan {
     int C, nseg, tiles;
-    size_t off_cnt1, off_cnt2, off_rec, off_part, off_seg, total;
+    size_t off_rec, off_part, off_seg, total;
 };
 
 static int env_int(const char* name, int dflt)
@@ -770,8 +791,6 @@ static bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* pl)
     pl->tiles = (pl->nseg + SPT - 1) / SPT;
     if (rows * C > INT_MAX || (int64_t)B * pl->tiles > INT_MAX) return false;
     size_t o = 0;
-    pl->off_cnt1 = o; o = align_up(o + sizeof(uint32_t) * (size_t)B, 256);
-    pl->off_cnt2 = o; o = align_up(o + sizeof(uint32_t) * (size_t)B, 256);
     pl->off_rec = o;  o = align_up(o + sizeof(SeqRec) * (size_t)B, 256);
     pl->off_part = o; o = align_up(o + sizeof(Partial) * (size_t)(rows * C), 256);
     pl->off_seg = o;  o = align_up(o + sizeof(float) * 2 * (size_t)B * (size_t)pl->nseg, 256);
@@ -821,8 +840,6 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->lse_p = diag ? diag->lse_p : nullptr;
     P->lse_q = diag ? diag->lse_q : nullptr;
     P->res_mass = diag ? diag->res_mass : nullptr;
-    P->cnt1 = reinterpret_cast<uint32_t*>(w + pl->off_cnt1);
-    P->cnt2 = reinterpret_cast<uint32_t*>(w + pl->off_cnt2);
     P->rec = reinterpret_cast<SeqRec*>(w + pl->off_rec);
     P->part = reinterpret_cast<Partial*>(w + pl->off_part);
     P->seg = reinterpret_cast<float*>(w + pl->off_seg);
@@ -839,16 +856,22 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
 static int launch_stats(const Params& P, const Plan& pl, int32_t dtype, hipStream_t st)
 {
     const dim3 grid((unsigned)((int64_t)P.B * (2 * P.K + 1) * pl.C));
-    if (dtype == SV_BF16) hipLaunchKernelGGL(k_stats<SV_BF16>, grid, dim3(NT), 0, st, P);
-    else hipLaunchKernelGGL(k_stats<SV_F32>, grid, dim3(NT), 0, st, P);
+    if (dtype == SV_BF16) hipLaunchKernelGGL(k_rowstats<SV_BF16>, grid, dim3(NT), 0, st, P);
+    else hipLaunchKernelGGL(k_rowstats<SV_F32>, grid, dim3(NT), 0, st, P);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
 }
 
 static int launch_draw(const Params& P, const Plan& pl, int32_t dtype, hipStream_t st)
 {
-    const dim3 grid((unsigned)((int64_t)P.B * pl.tiles));
-    if (dtype == SV_BF16) hipLaunchKernelGGL(k_draw<SV_BF16>, grid, dim3(NT), 0, st, P);
-    else hipLaunchKernelGGL(k_draw<SV_F32>, grid, dim3(NT), 0, st, P);
+    const dim3 grid_t((unsigned)((int64_t)P.B * pl.tiles));
+    const dim3 grid_b((unsigned)P.B);
+    if (dtype == SV_BF16) {
+        hipLaunchKernelGGL(k_decide<SV_BF16>, grid_t, dim3(NT), 0, st, P);
+        hipLaunchKernelGGL(k_search<SV_BF16>, grid_b, dim3(NT), 0, st, P);
+    } else {
+        hipLaunchKernelGGL(k_decide<SV_F32>, grid_t, dim3(NT), 0, st, P);
+        hipLaunchKernelGGL(k_search<SV_F32>, grid_b, dim3(NT), 0, st, P);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
 }
 
