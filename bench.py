@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the speculative-sampling verify step on one MI355X.
 
-One step = one spec_verify call (row statistics, acceptance tests, first
-rejection, final draw, emit) over one batch of synthetic logits already
+One step = one pass of the verify path (row statistics, acceptance tests,
+first rejection, final draw, emit) over one batch of synthetic logits already
 resident in HBM.  The default workload is the largest named one:
-B=256 sequences, K=8 draft tokens, V=152064 vocabulary, bf16 logits,
-T=1, sampling (target ~ N(0,4) + log-Zipf bias, draft = target + N(0,2.5)).
+B=256 sequences, K=8 draft tokens, V=152064 vocabulary, bf16 logits, T=1,
+sampling (target ~ N(0,4) + log-Zipf bias, draft = target + N(0,2.5)).
+`--config lmhead` times the fused LM-head workload instead (hidden bf16
+[32, 6, 4096] x W bf16 [4096, 128256] -> fp32 target logits, then the verify
+step against bf16 draft logits; one step = GEMM + verify).
 
-Prints one JSON line: verified logits/s (B*(K+1)*V per second), the roofline
-of the dominant kernel (k_rowstats: HBM-bound; algorithmic bytes = every target
-row and every draft row of sampling sequences read once, V*s bytes per row,
-divided by its average duration from HIP events recorded around it on the
-launch stream), and the fp64 oracle's throughput on this host as a CPU
-baseline.  Run `python bench.py --help` for options.
+Prints one JSON line: verified logits/s (B*(K+1)*V per second), the roofline of
+the dominant kernel (k_rowstats for the verify workloads: algorithmic bytes =
+every target row and every draft row of sampling sequences read once, V*s
+bytes per row; k_lmhead for the LM-head workload: the weight read once plus
+the hidden states and the fp32 logits, with its MFMA rate beside it), each
+divided by the kernel's average duration from HIP events recorded around it
+on the launch stream, and the fp64 oracle's throughput on this host as a CPU
+baseline.
 """
 
 from __future__ import annotations
@@ -31,26 +36,162 @@ if ROOT not in sys.path:
 
 METRIC = "verified logits/s (B·(K+1)·V per sec) + achieved HBM GB/s vs peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "speculative_sampling_verification_06_amd", "csrc", "spec_verify.hip")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_06_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+def _source_sha(name: str) -> str:
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
 
 
-def _traffic(workload_name: str):
-    """HBM bytes per k_rowstats launch from the committed PMC summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"k_rowstats_{workload_name}_traffic.txt")
+def _traffic(kernel: str, workload_name: str, source: str):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload_name}_traffic.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     tot = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not tot or sha.group(1) != _source_sha():
+    if not sha or not tot or sha.group(1) != _source_sha(source):
         return None
     return float(tot.group(1))
+
+
+def _timed(torch, stream, K, first, second):
+    """K steps of first() then second(), HIP events around each on the launch
+    stream; returns (host ms per step, first ms array, second ms array)."""
+    import numpy as np
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        evs[i][0].record(stream)
+        first()
+        evs[i][1].record(stream)
+        second()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    a = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
+    b = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
+    return (t1 - t0) * 1e3 / K, a, b
+
+
+def _base_result(w, K, warmup, ms_per_step, dtype_name):
+    return {
+        "metric": METRIC,
+        "value": w.verified_logits / (ms_per_step * 1e-3),
+        "unit": "logits/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+    }
+
+
+def _method_stats(w, acc):
+    import numpy as np
+    ok = acc >= 0
+    return {"accepted_len_hist": np.bincount(acc[ok], minlength=w.K + 1).tolist(),
+            "mean_accepted": float(acc[ok].mean()) if ok.any() else None,
+            "page_context": "pages quote 2-3x end-to-end decode speed-up, no hardware stated"}
+
+
+def bench_verify(args, torch, np, binding, I, dev):
+    w = I.CONFIGS[args.config]()
+    print(f"[bench] workload {w.name}: generated", file=sys.stderr, flush=True)
+    d = binding.to_device(w, dev)
+    a = (d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], d["greedy"])
+    call = binding.Bound(*a)                       # checks, outputs and workspace, once
+    out = call.verify()
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr, flush=True)
+        del src, dst
+    for _ in range(args.warmup):
+        call.stats()
+        call.draw()
+    ms, stats_ms, draw_ms = _timed(torch, stream, args.steps, call.stats, call.draw)
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    eager = I.eager_bytes(w)
+    acc = out["accepted_len"].cpu().numpy()
+    gpu = {k: v.cpu().numpy() for k, v in out.items()}
+    achieved = eager / (float(stats_ms.mean()) * 1e-3) / 1e9
+    step_ev = stats_ms + draw_ms
+    res = _base_result(w, args.steps, args.warmup, ms, "f32")
+    res["config"] = {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "logits": I.DTYPE_NAMES[w.dtype],
+                     "temperature": w.T, "greedy_sequences": int(w.greedy.sum()), "seed": w.seed,
+                     "verified_logits_per_step": w.verified_logits}
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS,
+                       "traffic": _traffic("k_rowstats", w.name, "spec_verify.hip"),
+                       "kernel": "k_rowstats", "algorithmic_bytes_per_launch": eager,
+                       "avg_launch_ms": float(stats_ms.mean())}
+    res["timing_ms"] = {"step_events_median": float(np.median(step_ev)),
+                        "step_events_p10": float(np.percentile(step_ev, 10)),
+                        "step_events_p90": float(np.percentile(step_ev, 90)),
+                        "k_rowstats_median": float(np.median(stats_ms)),
+                        "decide_search_median": float(np.median(draw_ms))}
+    res["method"] = _method_stats(w, acc)
+    needed = I.needed_bytes(w, acc)
+    res["method"].update(needed_bytes=needed, eager_bytes=eager, useful_bytes_fraction=needed / eager)
+    return w, gpu, res, None
+
+
+def bench_lmhead(args, torch, np, binding, I, dev):
+    w = I.cfg_lmhead()
+    print(f"[bench] workload {w.name}: generated", file=sys.stderr, flush=True)
+    M, d, V = w.B * (w.K + 1), w.hidden.shape[-1], w.V
+    hidden = binding.bf16_tensor(w.hidden, dev)
+    wt = binding.lmhead_pack(binding.bf16_tensor(w.w_lm, dev))   # static weight, packed once
+    dd = binding.to_device(w, dev)
+    logits = torch.empty(w.B, w.K + 1, V, dtype=torch.float32, device=dev)
+    gemm = binding.BoundLMHead(hidden.view(M, d), wt, logits.view(M, V))
+    gemm()
+    call = binding.Bound(logits, dd["draft"], dd["tokens"], dd["uniforms"], w.T, dd["greedy"])
+    out = call.verify()
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        gemm()
+        call.verify()
+    ms, gemm_ms, ver_ms = _timed(torch, stream, args.steps, gemm, call.verify)
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    acc = out["accepted_len"].cpu().numpy()
+    gpu = {k: v.cpu().numpy() for k, v in out.items()}
+    gemm_bytes = V * d * 2 + M * d * 2 + M * V * 4
+    flops = 2.0 * M * d * V
+    g_s = float(gemm_ms.mean()) * 1e-3
+    achieved = gemm_bytes / g_s / 1e9
+    res = _base_result(w, args.steps, args.warmup, ms, "bf16-mfma+f32")
+    res["config"] = {"workload": w.name, "B": w.B, "K": w.K, "V": V, "d": d,
+                     "logits": "f32 target / bf16 draft", "temperature": w.T, "seed": w.seed,
+                     "verified_logits_per_step": w.verified_logits}
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS,
+                       "traffic": _traffic("k_lmhead", w.name, "lmhead.hip"),
+                       "kernel": "k_lmhead", "algorithmic_bytes_per_launch": gemm_bytes,
+                       "avg_launch_ms": float(gemm_ms.mean()),
+                       "mfma_tflops": flops / g_s / 1e12,
+                       "mfma_frac": flops / g_s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    res["timing_ms"] = {"k_lmhead_median": float(np.median(gemm_ms)),
+                        "verify_median": float(np.median(ver_ms)),
+                        "step_events_median": float(np.median(gemm_ms + ver_ms))}
+    res["method"] = _method_stats(w, acc)
+    return w, gpu, res, "lmhead"
 
 
 def main() -> int:
@@ -58,7 +199,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="cfg152k", choices=["cfg152k", "cfg128k", "cfg32k", "tiny"])
+    ap.add_argument("--config", default="cfg152k", choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing (repeated whole-workload calls)")
@@ -85,101 +226,36 @@ def main() -> int:
     dev = torch.device("cuda:0")
     binding.load_library()
 
-    t_gen = time.perf_counter()
-    w = I.CONFIGS[args.config]()
-    gen_s = time.perf_counter() - t_gen
-    print(f"[bench] workload {w.name}: generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
-
-    d = binding.to_device(w, dev)
-    a = (d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], d["greedy"])
-    call = binding.Bound(*a)                       # checks, outputs and workspace, once
-    out = call.verify()
-    stream = torch.cuda.current_stream(dev)
-
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr, flush=True)
-        del src, dst
-
-    for _ in range(args.warmup):
-        call.stats()
-        call.draw()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        evs[i][0].record(stream)
-        call.stats()
-        evs[i][1].record(stream)
-        call.draw()
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
-
-    ms_per_step = (t1 - t0) * 1e3 / K
-    stats_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
-    draw_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
-    step_ev_ms = stats_ms + draw_ms
-
-    eager = I.eager_bytes(w)
-    acc = out["accepted_len"].cpu().numpy()
-    gpu = {k: v.cpu().numpy() for k, v in out.items()}
-    needed = I.needed_bytes(w, acc)
-    stats_avg_s = float(stats_ms.mean()) * 1e-3
-    achieved_gbs = eager / stats_avg_s / 1e9
-
-    result = {
-        "metric": METRIC,
-        "value": w.verified_logits / (ms_per_step * 1e-3),
-        "unit": "logits/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "logits": I.DTYPE_NAMES[w.dtype],
-                   "temperature": w.T, "greedy_sequences": int(w.greedy.sum()), "seed": w.seed,
-                   "verified_logits_per_step": w.verified_logits},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": _traffic(w.name),
-                     "kernel": "k_rowstats", "algorithmic_bytes_per_launch": eager,
-                     "avg_launch_ms": float(stats_ms.mean())},
-        "timing_ms": {"step_events_median": float(np.median(step_ev_ms)),
-                      "step_events_p10": float(np.percentile(step_ev_ms, 10)),
-                      "step_events_p90": float(np.percentile(step_ev_ms, 90)),
-                      "k_rowstats_median": float(np.median(stats_ms)),
-                      "decide_search_median": float(np.median(draw_ms))},
-        "method": {"accepted_len_hist": np.bincount(acc[acc >= 0], minlength=w.K + 1).tolist(),
-                   "mean_accepted": float(acc[acc >= 0].mean()) if (acc >= 0).any() else None,
-                   "needed_bytes": needed, "eager_bytes": eager,
-                   "useful_bytes_fraction": needed / eager,
-                   "page_context": "pages quote 2-3x end-to-end decode speed-up, no hardware stated"},
-    }
+    fn = bench_lmhead if args.config == "lmhead" else bench_verify
+    w, gpu, result, kind = fn(args, torch, np, binding, I, dev)
 
     if not args.no_cpu_baseline:
         import oracle
         from oracle import parity
         oracle.build(force=False)
         ncpu = len(os.sched_getaffinity(0))
-        med_s, used, calls = oracle.time_verify(w, reps=3, min_seconds=args.cpu_seconds, nthreads=ncpu)
-        result["cpu_baseline"] = {"value": w.verified_logits / med_s, "unit": "logits/s", "cores": used,
-                                  "kind": "oracle",
-                                  "sample": f"whole workload ({w.B} sequences), {calls} calls, median "
-                                            f"{med_s * 1e3:.1f} ms per call, fp64 C oracle, {used} threads"}
+        tgt = None
+        gemm_s = 0.0
+        if kind == "lmhead":
+            t0 = time.perf_counter()
+            tgt = oracle.lmhead_logits(w.hidden, w.w_lm)
+            gemm_s = time.perf_counter() - t0
+        t_start = time.perf_counter()
+        ts = []
+        orc = None
+        while len(ts) < 3 or time.perf_counter() - t_start < args.cpu_seconds:
+            t0 = time.perf_counter()
+            orc = oracle.verify(w, nthreads=ncpu, target=tgt)
+            ts.append(time.perf_counter() - t0)
+        med = float(np.median(ts))
+        sample = (f"whole workload ({w.B} sequences), {len(ts)} calls, median {med * 1e3:.1f} ms per call, "
+                  f"fp64 C oracle, {orc['nthreads']} threads")
+        if kind == "lmhead":
+            sample += f"; plus one fp64 numpy LM-head product of {gemm_s:.2f} s per step"
+        result["cpu_baseline"] = {"value": w.verified_logits / (med + gemm_s), "unit": "logits/s",
+                                  "cores": orc["nthreads"], "kind": "oracle", "sample": sample}
         try:
-            rep = parity.compare(w, gpu, oracle.verify(w, nthreads=ncpu))
+            rep = parity.compare(w, gpu, orc)
             result["parity"] = {"ok": True, "flagged": rep["flagged"],
                                 "flagged_mismatch": len(rep["flagged_mismatch"]), "invalid": rep["invalid"]}
         except parity.ParityError as e:

@@ -116,6 +116,16 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* spec_verify with separate storage types for the target and the draft
+ * logits (each SV_F32 or SV_BF16), e.g. fp32 target logits straight from an
+ * LM head with bf16 draft logits.  Same arguments, outputs and errors.      */
+int spec_verify_ex(const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, const float* uniforms,
+                   float temperature, const uint8_t* greedy_flag,
+                   int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype,
+                   int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* The same call in two parts, for timing and for checking the parts against
  * the whole: sv_stats streams every target row, and the draft rows of
  * sampling sequences, once into per-chunk
@@ -134,6 +144,35 @@ int sv_draw(const void* target_logits, const void* draft_logits,
             int32_t B, int32_t K, int32_t V, int32_t dtype,
             int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- fused LM head ------------------------------------------------------
+ * The target's last step maps each final hidden vector of d values to one
+ * score per vocabulary token ([QH] "Hidden state": the LM head turns the last
+ * hidden state into the table over the vocabulary).  The K+1 verify positions
+ * of B sequences share the weight:
+ *     target_logits[m, v] = sum_k hidden[m, k] * W[k, v]   (m < B*(K+1)),
+ * bf16 inputs, fp32 accumulation and output.
+ *
+ * sv_lmhead_pack: one-time repack of the static weight from W [d, V] (bf16,
+ *   row-major) into w_vd = W^T [V, d] (the [out_features, in_features]
+ *   layout), which the GEMM streams.  Both caller-owned device buffers.
+ *   EINVAL on d < 1, V < 1, NULL or misaligned (2 B) pointers.
+ * sv_lmhead: logits [M, V] fp32 = hidden [M, d] bf16 x W with w_vd [V, d]
+ *   bf16.  d must be a multiple of 8 and hidden / w_vd 16-byte aligned
+ *   (EINVAL otherwise); M == 0 is a no-op.
+ * spec_lmhead_verify: sv_lmhead on hidden [B, K+1, d] into the caller's
+ *   target_logits [B, K+1, V] fp32 buffer, then the verify step of
+ *   spec_verify on those logits with draft logits of draft_dtype.  Every
+ *   check of both parts runs before anything is launched; outputs, errors
+ *   and workspace as spec_verify (size it with dtype SV_F32).            */
+int sv_lmhead_pack(const void* w_dv, void* w_vd, int32_t d, int32_t V, void* stream);
+int sv_lmhead(const void* hidden, const void* w_vd, int32_t M, int32_t d, int32_t V,
+              float* logits, void* stream);
+int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* target_logits,
+                       const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
+                       const float* uniforms, float temperature, const uint8_t* greedy_flag,
+                       int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                       const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Short text for a return code (static storage). */
 const char* sv_strerror(int code);

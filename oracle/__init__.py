@@ -63,7 +63,7 @@ def _load():
         lib.oracle_draw.restype = C.c_int32
         lib.oracle_draw.argtypes = [C.c_void_p, C.c_int32, C.c_double, C.c_void_p, C.c_void_p]
         lib.oracle_verify.restype = C.c_int
-        lib.oracle_verify.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_double,
+        lib.oracle_verify.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_double,
                                       C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                       C.POINTER(_Diag), C.c_int]
         _lib = lib
@@ -118,10 +118,9 @@ def verify_arrays(target, draft, tokens, uniforms, T, greedy, B, K, V, nthreads=
     target = np.ascontiguousarray(target)
     dcode = _dtype_code(target)
     draft = None if draft is None else np.ascontiguousarray(draft)
-    if draft is not None and draft.size and draft.dtype != target.dtype:
-        raise TypeError("target and draft storage differ")
     if draft is not None and draft.size == 0:
         draft = None
+    ddcode = dcode if draft is None else _dtype_code(draft)
     tokens = np.ascontiguousarray(tokens, np.int32).reshape(B, K) if K > 0 else np.zeros((B, 0), np.int32)
     uniforms = np.ascontiguousarray(uniforms, np.float32).reshape(B, K + 1)
     g = None if greedy is None else np.ascontiguousarray(greedy, np.uint8)
@@ -137,7 +136,7 @@ def verify_arrays(target, draft, tokens, uniforms, T, greedy, B, K, V, nthreads=
                                         "test_margin", "draw_margin", "flags")])
     if nthreads is None:
         nthreads = len(os.sched_getaffinity(0))
-    rc = _load().oracle_verify(_ptr(target), _ptr(draft), dcode, _ptr(tokens) if K > 0 else None,
+    rc = _load().oracle_verify(_ptr(target), dcode, _ptr(draft), ddcode, _ptr(tokens) if K > 0 else None,
                                _ptr(uniforms), float(T), _ptr(g), B, K, V, _ptr(acc), _ptr(out),
                                C.byref(dg), int(nthreads))
     if rc != 0:

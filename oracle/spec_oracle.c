@@ -135,7 +135,7 @@ int32_t oracle_draw(const double* r, int32_t V, double u, double* S_out, double*
 /* ---- one sequence -------------------------------------------------------- */
 
 typedef struct {
-    const void* target; const void* draft; int dtype;
+    const void* target; const void* draft; int dtype; int ddtype;
     const int32_t* tokens; const float* uniforms; double T; const uint8_t* greedy;
     int32_t B, K, V;
     int32_t* acc; int32_t* out;
@@ -209,8 +209,8 @@ static void verify_sampling(const job_t* J, int32_t b, double* p, double* q, dou
         double lp, lq;
         if (!oracle_row_softmax(row_ptr(J->target, J->dtype, (size_t)b * (K + 1) + j, V),
                                 J->dtype, V, J->T, p, &lp)) { mark_invalid(J, b); return; }
-        if (!oracle_row_softmax(row_ptr(J->draft, J->dtype, (size_t)b * K + j, V),
-                                J->dtype, V, J->T, q, &lq)) { mark_invalid(J, b); return; }
+        if (!oracle_row_softmax(row_ptr(J->draft, J->ddtype, (size_t)b * K + j, V),
+                                J->ddtype, V, J->T, q, &lq)) { mark_invalid(J, b); return; }
         int32_t x = J->tokens[(size_t)b * K + j];
         if (x < 0 || x >= V || !u_ok(u[j])) { mark_invalid(J, b); return; }
         double px = p[x], qx = q[x];
@@ -296,13 +296,13 @@ static void* run_job(void* arg)
     return NULL;
 }
 
-int oracle_verify(const void* target, const void* draft, int dtype,
+int oracle_verify(const void* target, int dtype, const void* draft, int ddtype,
                   const int32_t* tokens, const float* uniforms, double T,
                   const uint8_t* greedy, int32_t B, int32_t K, int32_t V,
                   int32_t* accepted_len, int32_t* out_tokens,
                   const oracle_diag* diag, int nthreads)
 {
-    if (B < 0 || K < 0 || V < 1 || dtype < 0 || dtype > 2) return -1;
+    if (B < 0 || K < 0 || V < 1 || dtype < 0 || dtype > 2 || ddtype < 0 || ddtype > 2) return -1;
     if (B == 0) return 0;
     if (!target || !uniforms || !accepted_len || !out_tokens) return -1;
     if (K > 0 && !tokens) return -1;
@@ -319,7 +319,7 @@ int oracle_verify(const void* target, const void* draft, int dtype,
     if (!jobs || !th) { free(jobs); free(th); return -1; }
     int rc = 0;
     for (int t = 0; t < nthreads; ++t) {
-        job_t J = { target, draft, dtype, tokens, uniforms, T, greedy, B, K, V,
+        job_t J = { target, draft, dtype, ddtype, tokens, uniforms, T, greedy, B, K, V,
                     accepted_len, out_tokens, diag,
                     (int32_t)((int64_t)B * t / nthreads), (int32_t)((int64_t)B * (t + 1) / nthreads) };
         jobs[t] = J;

@@ -51,12 +51,13 @@ int oracle_row_argmax(const void* row, int dtype, int32_t V, int32_t* idx);
 int32_t oracle_draw(const double* r, int32_t V, double u, double* S, double* margin);
 
 /* The whole verify step for B sequences (see spec_oracle.c for the steps).
- * target [B,K+1,V], draft [B,K,V] (may be NULL when K == 0 or all greedy),
+ * target [B,K+1,V] stored as dtype, draft [B,K,V] stored as ddtype (may be
+ * NULL when K == 0 or all greedy),
  * tokens [B,K], uniforms [B,K+1] fp32, greedy [B] (NULL = all sampling).
  * Outputs accepted_len [B] (-1 = invalid input) and out_tokens [B,K+1]
  * (padding -1).  diag may be NULL; each of its pointers may be NULL.
  * nthreads <= 0 uses one thread.  Returns 0, or -1 on bad arguments. */
-int oracle_verify(const void* target, const void* draft, int dtype,
+int oracle_verify(const void* target, int dtype, const void* draft, int ddtype,
                   const int32_t* tokens, const float* uniforms, double T,
                   const uint8_t* greedy, int32_t B, int32_t K, int32_t V,
                   int32_t* accepted_len, int32_t* out_tokens,

@@ -21,7 +21,8 @@ SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_ELAUNCH = 0, -1, -2, -3
 SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
-EXPORTS = ("sv_workspace_bytes", "spec_verify", "sv_stats", "sv_draw", "sv_strerror", "sv_version")
+EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
+           "spec_lmhead_verify", "sv_strerror", "sv_version")
 
 
 class SvDiag(C.Structure):
@@ -56,12 +57,24 @@ def load_library(path: str = LIB_PATH):
                 fn = getattr(lib, name)
                 fn.restype = C.c_int
                 fn.argtypes = verify_args
+            lib.spec_verify_ex.restype = C.c_int
+            lib.spec_verify_ex.argtypes = verify_args[:10] + [C.c_int32] + verify_args[10:]
             lib.sv_workspace_bytes.restype = C.c_size_t
             lib.sv_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32]
             lib.sv_strerror.restype = C.c_char_p
             lib.sv_strerror.argtypes = [C.c_int]
             lib.sv_version.restype = C.c_int
             lib.sv_version.argtypes = []
+            lib.sv_lmhead_pack.restype = C.c_int
+            lib.sv_lmhead_pack.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
+            lib.sv_lmhead.restype = C.c_int
+            lib.sv_lmhead.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                      C.c_void_p]
+            lib.spec_lmhead_verify.restype = C.c_int
+            lib.spec_lmhead_verify.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                               C.c_int32, C.c_void_p, C.c_void_p, C.c_float, C.c_void_p,
+                                               C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                               C.POINTER(SvDiag), C.c_void_p, C.c_size_t, C.c_void_p]
             _lib = lib
     return _lib
 
@@ -137,9 +150,11 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
     dt = _dtype_code(target)
     dev = target.device
     _dev_ptr(target, "target_logits", shape=(B, K + 1, V))
+    ddt = dt
     if draft is not None:
-        if draft.dtype != target.dtype:
-            raise TypeError("draft logits must have the target's dtype")
+        ddt = _dtype_code(draft)
+        if ddt != dt and fn_name != "spec_verify":
+            raise TypeError("sv_stats / sv_draw need one storage type for target and draft logits")
         _dev_ptr(draft, "draft_logits", shape=(B, K, V))
     if tokens is not None:
         _dev_ptr(tokens, "draft_tokens", torch.int32, (B, K))
@@ -164,11 +179,14 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
     ws = workspace if workspace is not None else get_workspace(need, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    dts = (dt,) if ddt == dt else (dt, ddt)
+    if ddt != dt:
+        fn_name = "spec_verify_ex"
     rc = getattr(lib, fn_name)(
         target.data_ptr(), None if draft is None else draft.data_ptr(),
         None if tokens is None or tokens.numel() == 0 else tokens.data_ptr(),
         uniforms.data_ptr(), C.c_float(float(temperature)),
-        None if greedy is None else greedy.data_ptr(), B, K, V, dt,
+        None if greedy is None else greedy.data_ptr(), B, K, V, *dts,
         _dev_ptr(outputs["accepted_len"], "accepted_len", torch.int32, (B,)),
         _dev_ptr(outputs["out_tokens"], "out_tokens", torch.int32, (B, K + 1)),
         None if dg is None else C.byref(dg), ws.data_ptr(), ws.numel(), stream)
@@ -225,14 +243,16 @@ class Bound:
     def __init__(self, target, draft, tokens, uniforms, temperature, greedy=None, *,
                  outputs=None, diag=True, stream=None):
         torch = _torch()
+        mixed = draft is not None and draft.dtype != target.dtype
         # one checked call builds the outputs and the workspace
-        self.outputs = _call("sv_stats", target, draft, tokens, uniforms, temperature, greedy,
-                             outputs=outputs, diag=diag, stream=stream)
+        self.outputs = _call("spec_verify" if mixed else "sv_stats", target, draft, tokens, uniforms,
+                             temperature, greedy, outputs=outputs, diag=diag, stream=stream)
         torch.cuda.synchronize(target.device)
         lib = load_library()
         B, K1, V = target.shape
         K = K1 - 1
         dt = _dtype_code(target)
+        dts = (C.c_int32(dt),) if not mixed else (C.c_int32(dt), C.c_int32(_dtype_code(draft)))
         o = self.outputs
         self._dg = None
         if "p_tok" in o:
@@ -246,11 +266,15 @@ class Bound:
             C.c_void_p(None if tokens is None or tokens.numel() == 0 else tokens.data_ptr()),
             C.c_void_p(uniforms.data_ptr()), C.c_float(float(temperature)),
             C.c_void_p(None if greedy is None else greedy.data_ptr()),
-            C.c_int32(B), C.c_int32(K), C.c_int32(V), C.c_int32(dt),
+            C.c_int32(B), C.c_int32(K), C.c_int32(V), *dts,
             C.c_void_p(o["accepted_len"].data_ptr()), C.c_void_p(o["out_tokens"].data_ptr()),
             None if self._dg is None else C.byref(self._dg),
             C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel()), C.c_void_p(stream))
-        self._verify, self._stats, self._draw = lib.spec_verify, lib.sv_stats, lib.sv_draw
+        self.mixed = mixed
+        if mixed:
+            self._verify, self._stats, self._draw = lib.spec_verify_ex, None, None
+        else:
+            self._verify, self._stats, self._draw = lib.spec_verify, lib.sv_stats, lib.sv_draw
 
     def _check(self, rc):
         if rc != SV_OK:
@@ -261,9 +285,119 @@ class Bound:
         return self.outputs
 
     def stats(self):
+        if self._stats is None:
+            raise TypeError("the split launches need one storage type for target and draft logits")
         self._check(self._stats(*self._args))
         return self.outputs
 
     def draw(self):
+        if self._draw is None:
+            raise TypeError("the split launches need one storage type for target and draft logits")
         self._check(self._draw(*self._args))
         return self.outputs
+
+
+class BoundLMHead:
+    """The LM-head GEMM of one problem with pre-marshalled arguments."""
+
+    def __init__(self, hidden2d, w_vd, logits2d, stream=None):
+        torch = _torch()
+        M, d = hidden2d.shape
+        V = w_vd.shape[0]
+        _dev_ptr(hidden2d, "hidden", torch.bfloat16, (M, d))
+        _dev_ptr(w_vd, "w_vd", torch.bfloat16, (V, d))
+        _dev_ptr(logits2d, "logits", torch.float32, (M, V))
+        if stream is None:
+            stream = torch.cuda.current_stream(hidden2d.device).cuda_stream
+        self._keep = (hidden2d, w_vd, logits2d)
+        self._fn = load_library().sv_lmhead
+        self._args = (C.c_void_p(hidden2d.data_ptr()), C.c_void_p(w_vd.data_ptr()), C.c_int32(M), C.c_int32(d),
+                      C.c_int32(V), C.c_void_p(logits2d.data_ptr()), C.c_void_p(stream))
+
+    def __call__(self):
+        _check_rc(self._fn(*self._args))
+
+
+# ---------------------------------------------------------------- LM head --
+
+def _check_rc(rc):
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+
+
+def lmhead_pack(w_dv, out=None):
+    """One-time repack of the static LM-head weight W [d, V] bf16 into W^T [V, d]."""
+    torch = _torch()
+    d, V = w_dv.shape
+    _dev_ptr(w_dv, "w_dv", torch.bfloat16, (d, V))
+    if out is None:
+        out = torch.empty(V, d, dtype=torch.bfloat16, device=w_dv.device)
+    _dev_ptr(out, "w_vd", torch.bfloat16, (V, d))
+    _check_rc(load_library().sv_lmhead_pack(w_dv.data_ptr(), out.data_ptr(), d, V,
+                                            torch.cuda.current_stream(w_dv.device).cuda_stream))
+    return out
+
+
+def lmhead(hidden, w_vd, out=None):
+    """logits [M, V] fp32 = hidden [M, d] bf16 x W, with w_vd = W^T [V, d] bf16."""
+    torch = _torch()
+    M, d = hidden.shape
+    V = w_vd.shape[0]
+    _dev_ptr(hidden, "hidden", torch.bfloat16, (M, d))
+    _dev_ptr(w_vd, "w_vd", torch.bfloat16, (V, d))
+    if out is None:
+        out = torch.empty(M, V, dtype=torch.float32, device=hidden.device)
+    _dev_ptr(out, "logits", torch.float32, (M, V))
+    _check_rc(load_library().sv_lmhead(hidden.data_ptr(), w_vd.data_ptr(), M, d, V, out.data_ptr(),
+                                       torch.cuda.current_stream(hidden.device).cuda_stream))
+    return out
+
+
+def lmhead_verify(hidden, w_vd, draft, tokens, uniforms, temperature, greedy=None, *,
+                  target_logits=None, diag=True, stream=None):
+    """spec_lmhead_verify: the LM-head GEMM into target_logits [B, K+1, V] fp32,
+    then the verify step.  Returns Outputs (+ target_logits)."""
+    torch = _torch()
+    lib = load_library()
+    B, K1, d = hidden.shape
+    K = K1 - 1
+    V = w_vd.shape[0]
+    dev = hidden.device
+    _dev_ptr(hidden, "hidden", torch.bfloat16, (B, K + 1, d))
+    _dev_ptr(w_vd, "w_vd", torch.bfloat16, (V, d))
+    if draft is not None:
+        _dev_ptr(draft, "draft_logits", shape=(B, K, V))
+    if target_logits is None:
+        target_logits = torch.empty(B, K + 1, V, dtype=torch.float32, device=dev)
+    _dev_ptr(target_logits, "target_logits", torch.float32, (B, K + 1, V))
+    if tokens is not None:
+        _dev_ptr(tokens, "draft_tokens", torch.int32, (B, K))
+    _dev_ptr(uniforms, "uniforms", torch.float32, (B, K + 1))
+    o = Outputs(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                out_tokens=torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+    dg = None
+    if diag:
+        o.update(p_tok=torch.empty(B, K, device=dev), q_tok=torch.empty(B, K, device=dev),
+                 lse_p=torch.empty(B, K + 1, device=dev), lse_q=torch.empty(B, K, device=dev),
+                 res_mass=torch.empty(B, device=dev))
+        dg = SvDiag(*[o[k].data_ptr() for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
+    ws = get_workspace(lib.sv_workspace_bytes(B, K, V, SV_F32), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ddt = SV_F32 if draft is None else _dtype_code(draft)
+    _check_rc(lib.spec_lmhead_verify(
+        hidden.data_ptr(), w_vd.data_ptr(), d, target_logits.data_ptr(),
+        None if draft is None else draft.data_ptr(), ddt,
+        None if tokens is None or tokens.numel() == 0 else tokens.data_ptr(), uniforms.data_ptr(),
+        C.c_float(float(temperature)), None if greedy is None else greedy.data_ptr(), B, K, V,
+        o["accepted_len"].data_ptr(), o["out_tokens"].data_ptr(), None if dg is None else C.byref(dg),
+        ws.data_ptr(), ws.numel(), stream))
+    o["target_logits"] = target_logits
+    return o
+
+
+def bf16_tensor(bits, device):
+    """A torch bfloat16 device tensor from uint16 bf16 bits (numpy)."""
+    torch = _torch()
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)

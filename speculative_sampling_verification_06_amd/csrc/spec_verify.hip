@@ -40,6 +40,7 @@
 #include <string.h>
 
 #include "spec_verify.h"
+#include "sv_internal.h"
 
 namespace sv {
 
@@ -164,17 +165,25 @@ __device__ __forceinline__ float load1(const char* row, int64_t i)
     else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
 }
 
-// E consecutive elements starting at e (a multiple of E); -inf past V.
+// Eight consecutive elements starting at e (a multiple of 8); -inf past V.
+// One 16-byte load for bf16, two for fp32, when the row is 16-byte aligned.
+constexpr int LE = 8;                  // draw: elements per lane per segment
+constexpr int SEG = 64 * LE;           // draw: elements per segment (one wave)
+
 template <int DT>
-__device__ __forceinline__ void load_elems(const char* row, int64_t e, int64_t V, bool aligned, float* x)
+__device__ __forceinline__ void load8(const char* row, int64_t e, int64_t V, bool aligned, float* x)
 {
-    constexpr int E = Fmt<DT>::E;
-    if (aligned && e + E <= V) {
-        uint4 v = *reinterpret_cast<const uint4*>(row + e * Fmt<DT>::BYTES);
-        unpack<DT>(v, x);
+    if (aligned && e + LE <= V) {
+        const uint4* p = reinterpret_cast<const uint4*>(row + e * Fmt<DT>::BYTES);
+        if constexpr (DT == SV_BF16) {
+            unpack<SV_BF16>(p[0], x);
+        } else {
+            unpack<SV_F32>(p[0], x);
+            unpack<SV_F32>(p[1], x + 4);
+        }
     } else {
 #pragma unroll
-        for (int k = 0; k < E; ++k) x[k] = (e + k < V) ? load1<DT>(row, e + k) : NEG_INF;
+        for (int k = 0; k < LE; ++k) x[k] = (e + k < V) ? load1<DT>(row, e + k) : NEG_INF;
     }
 }
 
@@ -371,6 +380,30 @@ __device__ __forceinline__ void put(float* a, int64_t i, float v) { if (a) a[i] 
 // --------------------------------------------- k_rowstats: one row chunk --
 
 template <int DT>
+__device__ __forceinline__ void rowstats_body(const Params& P, const char* row, int64_t e0, int64_t e1,
+                                              bool greedy, Partial* dst, SmState* sh_sm, AmState* sh_am)
+{
+    SmState sm = {NEG_INF, 0.f};
+    AmState am = {NEG_INF, INT_MAX, 0u};
+    if (greedy) {
+        if (e0 < e1) scan_chunk<DT, true>(row, e0, e1, P.s, sm, am);
+        am = block_reduce_am(am, sh_am);
+        if (threadIdx.x == 0) *dst = {am.v, 0.f, am.i, am.bad};
+    } else {
+        if (e0 < e1) scan_chunk<DT, false>(row, e0, e1, P.s, sm, am);
+        sm = block_reduce_sm(sm, P.s, sh_sm);
+        if (threadIdx.x == 0) *dst = {sm.m, sm.z, 0, 0u};
+    }
+}
+
+// Chunk c of a row covers [c*cl, min((c+1)*cl, V)), cl a multiple of 8 elements.
+__device__ __forceinline__ int64_t chunk_len(int V, int C)
+{
+    const int64_t n8 = ((int64_t)V + 7) / 8;
+    return ((n8 + C - 1) / C) * 8;
+}
+
+template <int DTT, int DTD>
 __global__ __launch_bounds__(NT) void k_rowstats(const Params P)
 {
     const int K = P.K, R = 2 * K + 1;
@@ -385,24 +418,14 @@ __global__ __launch_bounds__(NT) void k_rowstats(const Params P)
     __shared__ AmState sh_am[NWAVE];
 
     if (is_draft && (greedy || P.draft == nullptr)) return;      // never read
-    const char* row = is_draft ? draft_row<DT>(P, b, r - K - 1) : target_row<DT>(P, b, r);
-    constexpr int E = Fmt<DT>::E;
-    const int64_t nvec = ((int64_t)P.V + E - 1) / E;
-    const int64_t cl = ((nvec + P.C - 1) / P.C) * E;              // chunk length, a multiple of E
+    const int64_t cl = chunk_len(P.V, P.C);
     const int64_t e0 = (int64_t)c * cl;
     const int64_t e1 = e0 + cl < (int64_t)P.V ? e0 + cl : (int64_t)P.V;
     Partial* dst = P.part + ((int64_t)b * R + r) * P.C + c;
-    SmState sm = {NEG_INF, 0.f};
-    AmState am = {NEG_INF, INT_MAX, 0u};
-    if (greedy) {
-        if (e0 < e1) scan_chunk<DT, true>(row, e0, e1, P.s, sm, am);
-        am = block_reduce_am(am, sh_am);
-        if (threadIdx.x == 0) *dst = {am.v, 0.f, am.i, am.bad};
-    } else {
-        if (e0 < e1) scan_chunk<DT, false>(row, e0, e1, P.s, sm, am);
-        sm = block_reduce_sm(sm, P.s, sh_sm);
-        if (threadIdx.x == 0) *dst = {sm.m, sm.z, 0, 0u};
-    }
+    if (is_draft)
+        rowstats_body<DTD>(P, draft_row<DTD>(P, b, r - K - 1), e0, e1, false, dst, sh_sm, sh_am);
+    else
+        rowstats_body<DTT>(P, target_row<DTT>(P, b, r), e0, e1, greedy, dst, sh_sm, sh_am);
 }
 
 // ------------------------------------------ decide: n for one sequence --
@@ -419,7 +442,7 @@ struct Decision {
 // write_out, also writes accepted_len, the accepted prefix, the greedy token,
 // the diagnostics and the record the search launch reads.  Every thread of the
 // workgroup must call it; *dec is valid for all threads on return.
-template <int DT>
+template <int DTT, int DTD>
 __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, Decision* dec)
 {
     const int K = P.K, V = P.V, C = P.C, R = 2 * K + 1;
@@ -470,8 +493,8 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
                 const bool u_ok = u >= 0.f && u < 1.f;
                 inval = !(f_ok[j] && f_ok[K + 1 + j] && tok_ok && u_ok);
                 if (!inval) {
-                    const float lx = load1<DT>(target_row<DT>(P, b, j), x);
-                    const float dx = load1<DT>(draft_row<DT>(P, b, j), x);
+                    const float lx = load1<DTT>(target_row<DTT>(P, b, j), x);
+                    const float dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
                     ptok = ex2(__builtin_fmaf(lx, s, -shift_of(f_m[j], s))) / f_z[j];
                     qtok = ex2(__builtin_fmaf(dx, s, -shift_of(f_m[K + 1 + j], s))) / f_z[K + 1 + j];
                     stop = !(u * qtok < ptok);            // accept iff u*q(x) < p(x)
@@ -559,26 +582,24 @@ __device__ __forceinline__ float weight(float l, float d, float s, float cp, flo
 // k_decide: one workgroup per (sequence b, tile t of the vocabulary).  Every
 // workgroup settles n itself (tile 0 also writes the outputs); sampling
 // sequences then sum the draw weights of row n over the tile's segments
-// (64*E elements, one per wave iteration) into the workspace.
-template <int DT>
+// (64*8 elements, one per wave iteration) into the workspace.
+template <int DTT, int DTD>
 __global__ __launch_bounds__(NT) void k_decide(const Params P)
 {
-    constexpr int E = Fmt<DT>::E;
-    constexpr int SEG = 64 * E;
     const int b = blockIdx.x / P.tiles;
     const int t = blockIdx.x - b * P.tiles;
     const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
     if (greedy && t > 0) return;
     __shared__ Decision dec;
-    decide_seq<DT>(P, b, greedy, t == 0, &dec);
+    decide_seq<DTT, DTD>(P, b, greedy, t == 0, &dec);
     if (greedy || !dec.ok) return;                  // uniform: dec is shared
 
     const int K = P.K, V = P.V, nseg = P.nseg;
     const float s = P.s;
     const int n = dec.n;
     const bool bonus = n == K;
-    const char* trow = target_row<DT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DT>(P, b, n);
+    const char* trow = target_row<DTT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
     const float cp = shift_of(dec.mp, s);
     const float cq = bonus ? 0.f : shift_of(dec.mq, s);
     const float w = bonus ? 0.f : dec.zp / dec.zq;
@@ -586,20 +607,20 @@ __global__ __launch_bounds__(NT) void k_decide(const Params P)
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
 
-    float xl[SPW][E], xd[SPW][E];
+    float xl[SPW][LE], xd[SPW][LE];
 #pragma unroll
     for (int k = 0; k < SPW; ++k) {
         const int seg = t * SPT + wave * SPW + k;
-        const int64_t e = (int64_t)seg * SEG + (int64_t)lane * E;
-        load_elems<DT>(trow, e, V, t_al, xl[k]);
-        if (!bonus) load_elems<DT>(drow, e, V, d_al, xd[k]);
+        const int64_t e = (int64_t)seg * SEG + (int64_t)lane * LE;
+        load8<DTT>(trow, e, V, t_al, xl[k]);
+        if (!bonus) load8<DTD>(drow, e, V, d_al, xd[k]);
     }
 #pragma unroll
     for (int k = 0; k < SPW; ++k) {
         const int seg = t * SPT + wave * SPW + k;
         float sr = 0.f, sp = 0.f;
 #pragma unroll
-        for (int q = 0; q < E; ++q) {
+        for (int q = 0; q < LE; ++q) {
             const float ep = ex2(__builtin_fmaf(xl[k][q], s, -cp));
             sp += ep;
             sr += bonus ? ep : weight(xl[k][q], xd[k][q], s, cp, cq, w, 0);
@@ -615,11 +636,9 @@ __global__ __launch_bounds__(NT) void k_decide(const Params P)
 
 // k_search: one workgroup per sequence.  Scans the segment sums for the one
 // segment holding u*S, then walks that segment lane by lane.
-template <int DT>
+template <int DTT, int DTD>
 __global__ __launch_bounds__(NT) void k_search(const Params P)
 {
-    constexpr int E = Fmt<DT>::E;
-    constexpr int SEG = 64 * E;
     const int b = blockIdx.x;
     const SeqRec rec = P.rec[b];
     if (rec.status != 1) return;
@@ -627,8 +646,8 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
     const float s = P.s;
     const int n = rec.n;
     const bool bonus = n == K;
-    const char* trow = target_row<DT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DT>(P, b, n);
+    const char* trow = target_row<DTT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
     const float cp = shift_of(rec.mp, s);
     const float cq = bonus ? 0.f : shift_of(rec.mq, s);
     const float w = bonus ? 0.f : rec.zp / rec.zq;
@@ -712,13 +731,13 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
     // Only a positive weight can be chosen; a segment with a positive sum
     // always holds one.
     if (wave == 0 && g >= 0) {
-        const int64_t e = (int64_t)g * SEG + (int64_t)lane * E;
-        float xl[E], xd[E], wv[E];
-        load_elems<DT>(trow, e, V, t_al, xl);
-        if (mode == 0) load_elems<DT>(drow, e, V, d_al, xd);
+        const int64_t e = (int64_t)g * SEG + (int64_t)lane * LE;
+        float xl[LE], xd[LE], wv[LE];
+        load8<DTT>(trow, e, V, t_al, xl);
+        if (mode == 0) load8<DTD>(drow, e, V, d_al, xd);
         float ls = 0.f;
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
+        for (int k = 0; k < LE; ++k) {
             wv[k] = weight(xl[k], mode == 0 ? xd[k] : 0.f, s, cp, cq, w, mode);
             ls += wv[k];
         }
@@ -727,7 +746,7 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
         float run = incl - ls;
         int cand = -1;
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
+        for (int k = 0; k < LE; ++k) {
             run += wv[k];
             if (cand < 0 && wv[k] > 0.f && run > thr2) cand = k;
         }
@@ -735,16 +754,16 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
         int y;
         if (m) {
             const int L = __ffsll((unsigned long long)m) - 1;
-            y = (int)((int64_t)g * SEG + (int64_t)L * E + __shfl(cand, L, 64));
+            y = (int)((int64_t)g * SEG + (int64_t)L * LE + __shfl(cand, L, 64));
         } else {
             int lastk = -1;
 #pragma unroll
-            for (int k = 0; k < E; ++k)
+            for (int k = 0; k < LE; ++k)
                 if (wv[k] > 0.f) lastk = k;
             const uint64_t mp = __ballot(lastk >= 0);
             const int L = mp ? 63 - __clzll((long long)mp) : 0;
             const int kk = __shfl(lastk, L, 64);
-            y = (int)((int64_t)g * SEG + (int64_t)L * E + (kk < 0 ? 0 : kk));
+            y = (int)((int64_t)g * SEG + (int64_t)L * LE + (kk < 0 ? 0 : kk));
         }
         if (lane == 0) {
             P.out[(int64_t)b * (K + 1) + n] = y;
@@ -771,13 +790,12 @@ static int env_int(const char* name, int dflt)
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* pl)
+static bool make_plan(int32_t B, int32_t K, int32_t V, Plan* pl)
 {
-    const int E = dtype == SV_BF16 ? Fmt<SV_BF16>::E : Fmt<SV_F32>::E;
     const int64_t R = 2 * (int64_t)K + 1;
     const int64_t rows = (int64_t)B * R;
-    const int64_t nvec = ((int64_t)V + E - 1) / E;
-    int64_t max_c = nvec / ((int64_t)NT * UNROLL);     // at least one full window per lane
+    const int64_t n8 = ((int64_t)V + 7) / 8;
+    int64_t max_c = n8 / ((int64_t)NT * UNROLL);        // at least one full window per lane
     if (max_c < 1) max_c = 1;
     static const int target_items = env_int("SV_TARGET_ITEMS", 4096);
     static const int forced_c = env_int("SV_CHUNKS", 0);
@@ -786,8 +804,7 @@ static bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* pl)
     if (C > max_c) C = max_c;
     if (C < 1) C = 1;
     pl->C = (int)C;
-    const int64_t seg = 64 * (int64_t)E;
-    pl->nseg = (int)(((int64_t)V + seg - 1) / seg);
+    pl->nseg = (int)(((int64_t)V + SEG - 1) / SEG);
     pl->tiles = (pl->nseg + SPT - 1) / SPT;
     if (rows * C > INT_MAX || (int64_t)B * pl->tiles > INT_MAX) return false;
     size_t o = 0;
@@ -800,23 +817,25 @@ static bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan* pl)
 
 static bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+static bool dtype_ok(int32_t dt) { return dt == SV_F32 || dt == SV_BF16; }
+static size_t dtype_bytes(int32_t dt) { return dt == SV_BF16 ? 2 : 4; }
+
 static int prepare(const void* target, const void* draft, const int32_t* tokens, const float* uniforms,
-                   float T, const uint8_t* greedy, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                   float T, const uint8_t* greedy, int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd,
                    int32_t* acc, int32_t* out, const sv_diag* diag, void* ws, size_t ws_bytes,
                    Params* P, Plan* pl)
 {
     (void)greedy;
     if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
-    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (!dtype_ok(dtt) || !dtype_ok(dtd)) return SV_EINVAL;
     if (!(T > 0.f) || !isfinite(T)) return SV_EINVAL;
     const double sd = 1.4426950408889634074 / (double)T;
     const float s = (float)sd;
     if (!isfinite(s) || !(s >= 1.17549435e-38f)) return SV_EINVAL;
     if (B == 0) return SV_OK;
-    const size_t es = dtype == SV_BF16 ? 2 : 4;
     if (!target || !uniforms || !acc || !out) return SV_EINVAL;
     if (K > 0 && !tokens) return SV_EINVAL;
-    if (!aligned_to(target, es) || (draft && !aligned_to(draft, es))) return SV_EINVAL;
+    if (!aligned_to(target, dtype_bytes(dtt)) || (draft && !aligned_to(draft, dtype_bytes(dtd)))) return SV_EINVAL;
     if (!aligned_to(uniforms, 4) || !aligned_to(acc, 4) || !aligned_to(out, 4) ||
         (tokens && !aligned_to(tokens, 4)))
         return SV_EINVAL;
@@ -825,7 +844,7 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
         for (const float* q : d)
             if (q && !aligned_to(q, 4)) return SV_EINVAL;
     }
-    if (!make_plan(B, K, V, dtype, pl)) return SV_EINVAL;
+    if (!make_plan(B, K, V, pl)) return SV_EINVAL;
     if (!ws || !aligned_to(ws, 16) || ws_bytes < pl->total) return SV_EWORKSPACE;
     char* w = static_cast<char*>(ws);
     P->target = target;
@@ -853,28 +872,61 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     return 1;   // ready to launch
 }
 
-static int launch_stats(const Params& P, const Plan& pl, int32_t dtype, hipStream_t st)
+template <int DTT, int DTD>
+static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
 {
     const dim3 grid((unsigned)((int64_t)P.B * (2 * P.K + 1) * pl.C));
-    if (dtype == SV_BF16) hipLaunchKernelGGL(k_rowstats<SV_BF16>, grid, dim3(NT), 0, st, P);
-    else hipLaunchKernelGGL(k_rowstats<SV_F32>, grid, dim3(NT), 0, st, P);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    hipLaunchKernelGGL((k_rowstats<DTT, DTD>), grid, dim3(NT), 0, st, P);
 }
 
-static int launch_draw(const Params& P, const Plan& pl, int32_t dtype, hipStream_t st)
+template <int DTT, int DTD>
+static void launch_draw_t(const Params& P, const Plan& pl, hipStream_t st)
 {
-    const dim3 grid_t((unsigned)((int64_t)P.B * pl.tiles));
-    const dim3 grid_b((unsigned)P.B);
-    if (dtype == SV_BF16) {
-        hipLaunchKernelGGL(k_decide<SV_BF16>, grid_t, dim3(NT), 0, st, P);
-        hipLaunchKernelGGL(k_search<SV_BF16>, grid_b, dim3(NT), 0, st, P);
-    } else {
-        hipLaunchKernelGGL(k_decide<SV_F32>, grid_t, dim3(NT), 0, st, P);
-        hipLaunchKernelGGL(k_search<SV_F32>, grid_b, dim3(NT), 0, st, P);
-    }
+    hipLaunchKernelGGL((k_decide<DTT, DTD>), dim3((unsigned)((int64_t)P.B * pl.tiles)), dim3(NT), 0, st, P);
+    hipLaunchKernelGGL((k_search<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
+}
+
+#define SV_DISPATCH(FN, dtt, dtd, ...)                                                         \
+    do {                                                                                       \
+        if (dtt == SV_BF16 && dtd == SV_BF16) FN<SV_BF16, SV_BF16>(__VA_ARGS__);               \
+        else if (dtt == SV_F32 && dtd == SV_F32) FN<SV_F32, SV_F32>(__VA_ARGS__);              \
+        else if (dtt == SV_F32 && dtd == SV_BF16) FN<SV_F32, SV_BF16>(__VA_ARGS__);            \
+        else FN<SV_BF16, SV_F32>(__VA_ARGS__);                                                 \
+    } while (0)
+
+static int launch_stats(const Params& P, const Plan& pl, int32_t dtt, int32_t dtd, hipStream_t st)
+{
+    SV_DISPATCH(launch_rowstats_t, dtt, dtd, P, pl, st);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
 }
 
+static int launch_draw(const Params& P, const Plan& pl, int32_t dtt, int32_t dtd, hipStream_t st)
+{
+    SV_DISPATCH(launch_draw_t, dtt, dtd, P, pl, st);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+}
+
+}  // namespace sv
+
+// Verify step with separate storage types for target and draft logits (the
+// fused LM-head path feeds fp32 target logits and bf16 draft logits).
+int sv_verify_mixed(const void* target, const void* draft, const int32_t* tokens, const float* uniforms,
+                    float T, const uint8_t* greedy, int32_t B, int32_t K, int32_t V, int32_t dtt,
+                    int32_t dtd, int32_t* acc, int32_t* out, const sv_diag* diag, void* ws,
+                    size_t ws_bytes, void* stream, int check_only)
+{
+    sv::Params P;
+    sv::Plan pl;
+    int rc = sv::prepare(target, draft, tokens, uniforms, T, greedy, B, K, V, dtt, dtd, acc, out, diag,
+                         ws, ws_bytes, &P, &pl);
+    if (rc <= 0 || check_only) return rc <= 0 ? rc : SV_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = sv::launch_stats(P, pl, dtt, dtd, st);
+    if (rc != SV_OK) return rc;
+    return sv::launch_draw(P, pl, dtt, dtd, st);
+}
+
+namespace sv {
 }  // namespace sv
 
 // ------------------------------------------------------------------ C ABI --
@@ -883,9 +935,9 @@ extern "C" {
 
 size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
 {
-    if (B <= 0 || K < 0 || K > SV_MAX_K || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return 0;
+    if (B <= 0 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(dtype)) return 0;
     sv::Plan pl;
-    if (!sv::make_plan(B, K, V, dtype, &pl)) return 0;
+    if (!sv::make_plan(B, K, V, &pl)) return 0;
     return pl.total;
 }
 
@@ -899,7 +951,7 @@ size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
     sv::Params P;                                                                              \
     sv::Plan pl;                                                                               \
     int rc = sv::prepare(target_logits, draft_logits, draft_tokens, uniforms, temperature,     \
-                         greedy_flag, B, K, V, dtype, accepted_len, out_tokens, diag,          \
+                         greedy_flag, B, K, V, dtype, dtype, accepted_len, out_tokens, diag,   \
                          workspace, workspace_bytes, &P, &pl);                                 \
     if (rc <= 0) return rc;                                                                    \
     hipStream_t st = static_cast<hipStream_t>(stream)
@@ -907,21 +959,32 @@ size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
 int spec_verify(SV_ARGS_DECL)
 {
     SV_PREPARE;
-    rc = sv::launch_stats(P, pl, dtype, st);
+    rc = sv::launch_stats(P, pl, dtype, dtype, st);
     if (rc != SV_OK) return rc;
-    return sv::launch_draw(P, pl, dtype, st);
+    return sv::launch_draw(P, pl, dtype, dtype, st);
 }
 
 int sv_stats(SV_ARGS_DECL)
 {
     SV_PREPARE;
-    return sv::launch_stats(P, pl, dtype, st);
+    return sv::launch_stats(P, pl, dtype, dtype, st);
+}
+
+int spec_verify_ex(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                   const float* uniforms, float temperature, const uint8_t* greedy_flag, int32_t B, int32_t K,
+                   int32_t V, int32_t target_dtype, int32_t draft_dtype, int32_t* accepted_len,
+                   int32_t* out_tokens, const sv_diag* diag, void* workspace, size_t workspace_bytes,
+                   void* stream)
+{
+    return sv_verify_mixed(target_logits, draft_logits, draft_tokens, uniforms, temperature, greedy_flag, B, K,
+                           V, target_dtype, draft_dtype, accepted_len, out_tokens, diag, workspace,
+                           workspace_bytes, stream, 0);
 }
 
 int sv_draw(SV_ARGS_DECL)
 {
     SV_PREPARE;
-    return sv::launch_draw(P, pl, dtype, st);
+    return sv::launch_draw(P, pl, dtype, dtype, st);
 }
 
 const char* sv_strerror(int code)

@@ -102,3 +102,40 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+@pytest.mark.parametrize("M,d,V,h,w,out", [
+    (4, 12, 100, FAKE, FAKE, FAKE),        # d not a multiple of 8
+    (4, 0, 100, FAKE, FAKE, FAKE),
+    (4, 16, 0, FAKE, FAKE, FAKE),
+    (-1, 16, 100, FAKE, FAKE, FAKE),
+    (4, 16, 100, FAKE + 8, FAKE, FAKE),    # hidden not 16-byte aligned
+    (4, 16, 100, FAKE, FAKE + 2, FAKE),
+    (4, 16, 100, FAKE, FAKE, FAKE + 2),
+    (4, 16, 100, None, FAKE, FAKE),
+])
+def test_lmhead_host_checks(lib, M, d, V, h, w, out):
+    assert lib.sv_lmhead(h, w, M, d, V, out, None) == binding.SV_EINVAL
+
+
+def test_lmhead_empty_is_a_no_op(lib):
+    assert lib.sv_lmhead(None, None, 0, 16, 100, None, None) == binding.SV_OK
+
+
+def test_lmhead_pack_host_checks(lib):
+    assert lib.sv_lmhead_pack(FAKE, FAKE, 0, 10, None) == binding.SV_EINVAL
+    assert lib.sv_lmhead_pack(FAKE + 1, FAKE, 16, 10, None) == binding.SV_EINVAL
+    assert lib.sv_lmhead_pack(None, FAKE, 16, 10, None) == binding.SV_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(draft_dtype=5), dict(T=0.0), dict(K=64), dict(d=12),
+                                dict(ws_bytes=16), dict(uniforms=None)])
+def test_fused_verify_checks_everything_before_launch(lib, kw):
+    a = dict(hidden=FAKE, w=FAKE, d=16, logits=FAKE, draft=FAKE, draft_dtype=1, tokens=FAKE,
+             uniforms=FAKE, T=1.0, greedy=None, B=2, K=3, V=100, acc=FAKE, out=FAKE, diag=None,
+             ws=FAKE, ws_bytes=binding.workspace_bytes(2, 3, 100, 0))
+    a.update(kw)
+    rc = lib.spec_lmhead_verify(a["hidden"], a["w"], a["d"], a["logits"], a["draft"], a["draft_dtype"],
+                                a["tokens"], a["uniforms"], C.c_float(a["T"]), a["greedy"], a["B"], a["K"],
+                                a["V"], a["acc"], a["out"], a["diag"], a["ws"], a["ws_bytes"], None)
+    assert rc in (binding.SV_EINVAL, binding.SV_EWORKSPACE)

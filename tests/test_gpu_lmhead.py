@@ -1,0 +1,99 @@
+"""GPU parity of the fused LM head: repack, MFMA GEMM and the fused verify.
+
+The GEMM is compared with the oracle's fp64 product of the same bf16 values.
+Bound: bf16 x bf16 products are exact in fp32, and any order of d - 1 fp32
+additions stays within d * 2^-24 * sum_k |h_k w_k| of the exact sum; the test
+uses that worst-case bound (observed errors are far below it).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import parity
+from speculative_sampling_verification_06_amd import binding
+from speculative_sampling_verification_06_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+    oracle.build(force=False)
+    return torch.device("cuda:0")
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _rand_bf16(rng, shape, scale):
+    return I.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+
+@pytest.mark.parametrize("d,V", [(1, 1), (70, 333), (4096, 130)])
+def test_pack_is_a_transpose(dev, d, V):
+    import torch
+    rng = np.random.default_rng(d + V)
+    w = _rand_bf16(rng, (d, V), 1.0)
+    wt = binding.lmhead_pack(binding.bf16_tensor(w, dev))
+    torch.cuda.synchronize()
+    got = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, w.T)
+
+
+@pytest.mark.parametrize("M,d,V", [(1, 8, 1), (5, 24, 33), (192, 256, 1000), (200, 4096, 515),
+                                   (37, 4104, 300), (192, 4096, 4100)])
+def test_gemm_against_fp64_product(dev, M, d, V):
+    import torch
+    _log(f"[lmhead] gemm M={M} d={d} V={V}")
+    rng = np.random.default_rng(M * 7 + d + V)
+    h = _rand_bf16(rng, (M, d), 1.0)
+    w = _rand_bf16(rng, (d, V), 0.02)
+    wt = binding.lmhead_pack(binding.bf16_tensor(w, dev))
+    got = binding.lmhead(binding.bf16_tensor(h, dev), wt)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    want = oracle.lmhead_logits(h.reshape(1, M, d), w)[0]
+    habs = np.abs(I.bf16_bits_to_f32(h).astype(np.float64))
+    wabs = np.abs(I.bf16_bits_to_f32(w).astype(np.float64))
+    bound = d * U32 * (habs @ wabs)
+    err = np.abs(got - want)
+    _log(f"[lmhead] max err {err.max():.3g}, max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}")
+    assert np.all(err <= bound)
+
+
+def test_gemm_rejects_bad_shapes(dev):
+    import torch
+    h = torch.zeros(4, 12, dtype=torch.bfloat16, device=dev)
+    wt = torch.zeros(8, 12, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(binding.SpecVerifyError):
+        binding.lmhead(h, wt)          # d = 12 is not a multiple of 8
+
+
+def test_fused_lmhead_verify_full_size(dev):
+    import torch
+    w = I.cfg_lmhead()
+    _log(f"[lmhead] {w.name}: generated")
+    d_h = binding.bf16_tensor(w.hidden, dev)
+    wt = binding.lmhead_pack(binding.bf16_tensor(w.w_lm, dev))
+    dd = binding.to_device(w, dev)
+    out = binding.lmhead_verify(d_h, wt, dd["draft"], dd["tokens"], dd["uniforms"], w.T, dd["greedy"])
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    tgt64 = oracle.lmhead_logits(w.hidden, w.w_lm)
+    err = np.abs(g["target_logits"].astype(np.float64) - tgt64)
+    _log(f"[lmhead] logits max abs err {err.max():.3g}")
+    o = oracle.verify(w, target=tgt64)
+    rep = parity.compare(w, g, o)
+    _log(f"[lmhead] verify parity {rep}")
+    assert err.max() < 1e-3

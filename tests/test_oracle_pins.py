@@ -398,3 +398,24 @@ def test_accepted_prefix_and_padding_layout():
         assert np.all(r.out_tokens[b, n + 1:] == -1)
         assert np.all(np.isfinite(r.p_tok[b, :min(n + 1, w.K)]))
         assert np.all(np.isnan(r.p_tok[b, n + 1:]))
+
+
+# ---------------------------------------------------------------------------
+# LM-head product: exact on integer-valued bf16 inputs
+# ---------------------------------------------------------------------------
+
+def test_lmhead_product_exact_on_integers():
+    """Small integers are exact in bf16 and their fp64 dot products are exact, so
+    the oracle's product must equal the integer matmul exactly (a transposed
+    operand or a wrong axis fails)."""
+    rng = np.random.default_rng(4)
+    B, K1, d, V = 3, 4, 40, 57
+    h = rng.integers(-8, 9, size=(B, K1, d))
+    w = rng.integers(-8, 9, size=(d, V))
+    hb = I.f32_to_bf16_bits(h.astype(np.float32))
+    wb = I.f32_to_bf16_bits(w.astype(np.float32))
+    got = oracle.lmhead_logits(hb, wb, col_block=16)
+    want = np.einsum("bkd,dv->bkv", h.astype(object), w.astype(object)).astype(np.float64)
+    assert np.array_equal(got, want)
+    sub = oracle.lmhead_logits(hb, wb, rows=[2, 0])
+    assert np.array_equal(sub, want[[2, 0]])
