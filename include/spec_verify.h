@@ -174,6 +174,20 @@ int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* t
                        int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
                        const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Row-statistics schedule, process-wide (thread-safe; a tuning knob, it never
+ * changes a decision):
+ *   SV_MODE_AUTO  per call: lazy when one eager pass would stream >= 32 MiB
+ *   SV_MODE_EAGER one launch streams every row of every position
+ *   SV_MODE_LAZY  one launch per position streams it only for sequences that
+ *                 reach it (rows past the first rejection are never read)
+ * The environment variable SV_MODE=eager|lazy sets the initial value.
+ * sv_set_mode returns SV_EINVAL for other values.                          */
+#define SV_MODE_AUTO  0
+#define SV_MODE_EAGER 1
+#define SV_MODE_LAZY  2
+int sv_set_mode(int mode);
+int sv_get_mode(void);
+
 /* Short text for a return code (static storage). */
 const char* sv_strerror(int code);
 

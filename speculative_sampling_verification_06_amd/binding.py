@@ -22,7 +22,8 @@ SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
-           "spec_lmhead_verify", "sv_strerror", "sv_version")
+           "spec_lmhead_verify", "sv_set_mode", "sv_get_mode", "sv_strerror", "sv_version")
+MODE_AUTO, MODE_EAGER, MODE_LAZY = 0, 1, 2
 
 
 class SvDiag(C.Structure):
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
             lib.sv_strerror.argtypes = [C.c_int]
             lib.sv_version.restype = C.c_int
             lib.sv_version.argtypes = []
+            lib.sv_set_mode.restype = C.c_int
+            lib.sv_set_mode.argtypes = [C.c_int]
+            lib.sv_get_mode.restype = C.c_int
+            lib.sv_get_mode.argtypes = []
             lib.sv_lmhead_pack.restype = C.c_int
             lib.sv_lmhead_pack.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
             lib.sv_lmhead.restype = C.c_int
@@ -85,6 +90,17 @@ def strerror(code: int) -> str:
 
 def workspace_bytes(B: int, K: int, V: int, dtype: int) -> int:
     return int(load_library().sv_workspace_bytes(B, K, V, dtype))
+
+
+def set_mode(mode: int) -> None:
+    """Row-statistics schedule for later calls: MODE_AUTO, MODE_EAGER or MODE_LAZY."""
+    rc = load_library().sv_set_mode(int(mode))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+
+
+def get_mode() -> int:
+    return int(load_library().sv_get_mode())
 
 
 # ------------------------------------------------------------------ torch --

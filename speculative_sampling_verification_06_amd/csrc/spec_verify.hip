@@ -2,25 +2,31 @@
 // verify step.  Page citations ([QH], [NL], [MC]) are spelled out in
 // include/spec_verify.h next to the declarations.
 //
-// Three launches on the caller's stream; kernel boundaries are the only
+// Launches on the caller's stream; kernel boundaries are the only
 // synchronisation between workgroups (no fences, no counters):
 //
-//   k_rowstats  one workgroup per (sequence b, row r, vocab chunk c).  Rows
-//               r = 0..K are target rows, r = K+1..2K draft rows.  The chunk
-//               is streamed once with 16-byte loads (UNROLL in flight per
-//               lane); sampling rows keep an online softmax state (running max
-//               m and sum z of exp2(x*s - m*s), s = log2(e)/T), greedy rows a
-//               lowest-index argmax.  One 16-byte partial per chunk goes to
-//               the workspace.  This is the HBM stream: every logit once.
-//   k_decide    one workgroup per (sequence b, vocab tile t).  Each merges the
-//               sequence's partials in chunk order, runs the K acceptance tests
-//               on wave 0 and finds the first rejection n with one ballot;
-//               tile 0 writes accepted_len, the accepted prefix, the greedy
-//               token and the diagnostics.  Sampling sequences then sum the
-//               draw weights of row n (residual max(0, p - q) scaled by Z_p, or
-//               p for the bonus) per 64*E-element segment of the tile.
-//   k_search    one workgroup per sampling sequence: scans the segment sums
-//               for u*S, re-reads that one segment and walks it lane by lane.
+//   row statistics, one of two schedules:
+//   k_rowstats       eager: one launch, one workgroup per (sequence b, row r,
+//                    vocab chunk c); rows r = 0..K are target rows, K+1..2K
+//                    draft rows.
+//   k_rowstats_lazy  lazy: one launch per position j = 0..K, rows of position
+//                    j only for sequences that reach j (rows past the first
+//                    rejection are never read).
+//                    Either way a workgroup streams its chunk once with
+//                    16-byte loads (UNROLL in flight per lane); sampling rows
+//                    keep an online softmax state (running max m and sum z of
+//                    exp2(x*s - m*s), s = log2(e)/T), greedy rows a
+//                    lowest-index argmax; one 16-byte partial per chunk.
+//   k_decide         one workgroup per sequence: merges the partials in chunk
+//                    order, runs the K tests on wave 0 and finds the first
+//                    rejection n with one ballot; writes accepted_len, the
+//                    accepted prefix, the greedy token, the diagnostics and a
+//                    record for the draw.
+//   k_tiles          one workgroup per (sampling sequence, vocab tile): draw
+//                    weights of row n (residual max(0, p - q) scaled by Z_p, or
+//                    p for the bonus) summed per 512-element segment.
+//   k_search         one workgroup per sampling sequence: scans the segment
+//                    sums for u*S, re-reads that one segment, walks it.
 //
 // Numerics: every term is exp2(fma(x, s, -c)) with c = m*s held as an exact
 // shift, so the row's own rounding of c cancels out of every ratio; partial
@@ -38,6 +44,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "spec_verify.h"
 #include "sv_internal.h"
@@ -95,6 +103,7 @@ struct Params {
     float* res_mass;
     Partial* part;
     SeqRec* rec;
+    int32_t* reach;   // lazy mode: last position each sequence was seen alive at
     float* seg;       // [2][B][nseg]: residual sums, then p sums
     int32_t B, K, V, C;
     int32_t nseg, tiles;
@@ -442,37 +451,83 @@ struct Decision {
 // write_out, also writes accepted_len, the accepted prefix, the greedy token,
 // the diagnostics and the record the search launch reads.  Every thread of the
 // workgroup must call it; *dec is valid for all threads on return.
+// Merged statistics of one row from its C chunk partials, always in chunk
+// order (every caller gets the same bits).
+struct RowStat {
+    float m, z;       // softmax: running max and sum; greedy: max value (z unused)
+    int32_t i;        // greedy: lowest index of the max
+    int32_t ok;       // row valid
+};
+
+// Partials are loaded eight at a time (independent loads, one round trip)
+// and merged in chunk order.
+constexpr int MERGE_BATCH = 8;
+
+__device__ __forceinline__ RowStat merge_row(const Partial* pp, int C, float s, bool greedy)
+{
+    AmState am = {NEG_INF, INT_MAX, 0u};
+    SmState sm = {NEG_INF, 0.f};
+    for (int c0 = 0; c0 < C; c0 += MERGE_BATCH) {
+        Partial t[MERGE_BATCH];
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u)
+            if (c0 + u < C) t[u] = pp[c0 + u];
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u) {
+            if (c0 + u < C) {
+                if (greedy) am = am_merge(am, {t[u].m, t[u].idx, t[u].bad});
+                else sm = sm_merge(sm, {t[u].m, t[u].z}, s);
+            }
+        }
+    }
+    if (greedy) return {am.v, 0.f, am.i, (am.bad == 0u) && am.v > NEG_INF && am.v < POS_INF};
+    return {sm.m, sm.z, 0, (sm.z > 0.f) && (sm.z < POS_INF) && sm.m > NEG_INF && sm.m < POS_INF};
+}
+
+struct TestOut {
+    bool stop, inval;
+    float ptok, qtok;
+};
+
+// The test at position j (j < K): greedy keeps x_j iff it is the lowest-index
+// argmax of target row j; sampling keeps it iff u_j * q_j(x_j) < p_j(x_j).
+// stop = rejected or invalid.  t, d: merged target row j and draft row j.
+template <int DTT, int DTD>
+__device__ __forceinline__ TestOut position_test(const Params& P, int b, int j, bool greedy, const RowStat& t,
+                                                 const RowStat& d, int32_t x, float u)
+{
+    const float s = P.s;
+    TestOut o = {true, true, NAN, NAN};
+    const bool tok_ok = x >= 0 && x < P.V;
+    if (greedy) {
+        o.inval = !(t.ok && tok_ok);
+        o.stop = o.inval || x != t.i;
+        return o;
+    }
+    const bool u_ok = u >= 0.f && u < 1.f;
+    o.inval = !(t.ok && d.ok && tok_ok && u_ok);
+    if (o.inval) return o;
+    const float lx = load1<DTT>(target_row<DTT>(P, b, j), x);
+    const float dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
+    o.ptok = ex2(__builtin_fmaf(lx, s, -shift_of(t.m, s))) / t.z;
+    o.qtok = ex2(__builtin_fmaf(dx, s, -shift_of(d.m, s))) / d.z;
+    o.stop = !(u * o.qtok < o.ptok);
+    return o;
+}
+
 template <int DTT, int DTD>
 __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, Decision* dec)
 {
-    const int K = P.K, V = P.V, C = P.C, R = 2 * K + 1;
+    const int K = P.K, C = P.C, R = 2 * K + 1;
     const float s = P.s;
     const int tid = threadIdx.x;
-    __shared__ float f_m[MAXR], f_z[MAXR];
-    __shared__ int32_t f_i[MAXR];
-    __shared__ int32_t f_ok[MAXR];
+    __shared__ RowStat f_rs[MAXR];
 
     if (tid < R) {
         const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
-        if (greedy) {
-            if (tid <= K) {
-                AmState a = {NEG_INF, INT_MAX, 0u};
-                for (int c = 0; c < C; ++c) a = am_merge(a, {pp[c].m, pp[c].idx, pp[c].bad});
-                f_m[tid] = a.v;
-                f_i[tid] = a.i;
-                f_ok[tid] = (a.bad == 0u) && a.v > NEG_INF && a.v < POS_INF;
-            } else {
-                f_ok[tid] = 0;
-            }
-        } else if (tid <= K || P.draft != nullptr) {
-            SmState a = {NEG_INF, 0.f};
-            for (int c = 0; c < C; ++c) a = sm_merge(a, {pp[c].m, pp[c].z}, s);
-            f_m[tid] = a.m;
-            f_z[tid] = a.z;
-            f_ok[tid] = (a.z > 0.f) && (a.z < POS_INF) && a.m > NEG_INF && a.m < POS_INF;
-        } else {
-            f_ok[tid] = 0;
-        }
+        const bool draft_row_ = tid > K;
+        if (draft_row_ && (greedy || P.draft == nullptr)) f_rs[tid] = {0.f, 0.f, 0, 0};
+        else f_rs[tid] = merge_row(pp, C, s, greedy);
     }
     __syncthreads();
 
@@ -484,31 +539,19 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         int32_t x = -1;
         if (j < K) {
             x = P.tokens[(int64_t)b * K + j];
-            const bool tok_ok = x >= 0 && x < V;
-            if (greedy) {
-                inval = !(f_ok[j] && tok_ok);
-                stop = inval || x != f_i[j];
-            } else {
-                const float u = P.uniforms[ub + j];
-                const bool u_ok = u >= 0.f && u < 1.f;
-                inval = !(f_ok[j] && f_ok[K + 1 + j] && tok_ok && u_ok);
-                if (!inval) {
-                    const float lx = load1<DTT>(target_row<DTT>(P, b, j), x);
-                    const float dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
-                    ptok = ex2(__builtin_fmaf(lx, s, -shift_of(f_m[j], s))) / f_z[j];
-                    qtok = ex2(__builtin_fmaf(dx, s, -shift_of(f_m[K + 1 + j], s))) / f_z[K + 1 + j];
-                    stop = !(u * qtok < ptok);            // accept iff u*q(x) < p(x)
-                } else {
-                    stop = true;
-                }
-            }
+            const float u = greedy ? 0.f : P.uniforms[ub + j];
+            const TestOut o = position_test<DTT, DTD>(P, b, j, greedy, f_rs[j], f_rs[K + 1 + j], x, u);
+            stop = o.stop;
+            inval = o.inval;
+            ptok = o.ptok;
+            qtok = o.qtok;
         }
         const uint64_t smask = __ballot(stop);
         const uint64_t imask = __ballot(inval);
         const int n = smask ? (__ffsll((unsigned long long)smask) - 1) : K;
         bool bad = (n < K) && ((imask >> n) & 1ull);
         float uK = 0.f;
-        if (!bad && n == K) bad = !f_ok[K];
+        if (!bad && n == K) bad = !f_rs[K].ok;
         if (!bad && !greedy) {
             uK = P.uniforms[ub + K];
             bad = !(uK >= 0.f && uK < 1.f);
@@ -516,10 +559,10 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         if (j == 0) {
             dec->n = n;
             dec->ok = !bad;
-            dec->mp = bad || greedy ? 0.f : f_m[n];
-            dec->zp = bad || greedy ? 1.f : f_z[n];
-            dec->mq = (bad || greedy || n == K) ? 0.f : f_m[K + 1 + n];
-            dec->zq = (bad || greedy || n == K) ? 1.f : f_z[K + 1 + n];
+            dec->mp = bad || greedy ? 0.f : f_rs[n].m;
+            dec->zp = bad || greedy ? 1.f : f_rs[n].z;
+            dec->mq = (bad || greedy || n == K) ? 0.f : f_rs[K + 1 + n].m;
+            dec->zq = (bad || greedy || n == K) ? 1.f : f_rs[K + 1 + n].z;
             dec->u = uK;
         }
         if (write_out) {
@@ -537,15 +580,15 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
                     put(P.res_mass, b, NAN);
                 }
             } else {
-                if (j <= K) out[j] = (j < n) ? x : ((j == n && greedy) ? f_i[n] : -1);
+                if (j <= K) out[j] = (j < n) ? x : ((j == n && greedy) ? f_rs[n].i : -1);
                 const bool seen = !greedy && j <= n;
                 if (j < K) {
                     put(P.p_tok, (int64_t)b * K + j, seen ? ptok : NAN);
                     put(P.q_tok, (int64_t)b * K + j, seen ? qtok : NAN);
                     put(P.lse_q, (int64_t)b * K + j,
-                        seen ? (shift_of(f_m[K + 1 + j], s) + log2f(f_z[K + 1 + j])) * LN2 : NAN);
+                        seen ? (shift_of(f_rs[K + 1 + j].m, s) + log2f(f_rs[K + 1 + j].z)) * LN2 : NAN);
                 }
-                if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_m[j], s) + log2f(f_z[j])) * LN2 : NAN);
+                if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_rs[j].m, s) + log2f(f_rs[j].z)) * LN2 : NAN);
                 if (j == 0) {
                     P.acc[b] = n;
                     if (greedy) put(P.res_mass, b, 0.f);
@@ -555,10 +598,10 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
                 SeqRec r;
                 r.n = n;
                 r.status = (!bad && !greedy) ? 1 : 0;
-                r.mp = f_m[n];
-                r.zp = greedy ? 1.f : f_z[n];
-                r.mq = (greedy || n == K) ? 0.f : f_m[K + 1 + n];
-                r.zq = (greedy || n == K) ? 1.f : f_z[K + 1 + n];
+                r.mp = f_rs[n].m;
+                r.zp = greedy ? 1.f : f_rs[n].z;
+                r.mq = (greedy || n == K) ? 0.f : f_rs[K + 1 + n].m;
+                r.zq = (greedy || n == K) ? 1.f : f_rs[K + 1 + n].z;
                 r.u = uK;
                 r.pad = 0;
                 P.rec[b] = r;
@@ -566,6 +609,64 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         }
     }
     __syncthreads();
+}
+
+// --------------------------- k_rowstats_lazy: position j, live rows only --
+//
+// Lazy mode streams position j only for sequences that reach it, in one launch
+// per position (j = 0..K): the method never examines rows after the first
+// rejection, so they are never read.  Grid: B x (2 rows, or 1 at j = K) x C.
+// A workgroup first settles whether its sequence reaches j: reach[b] (written
+// by launch j-1) says position j-1 was streamed, and thread 0 re-runs the test
+// at j-1 from that position's partials with the same merge and test code
+// k_decide uses, so the two can never disagree.
+
+template <int DTT, int DTD>
+__device__ bool reaches(const Params& P, int b, int j, bool greedy)
+{
+    if (j == 0) return true;
+    // most sequences are gone after a few positions: one load settles those
+    if (P.reach[b] < j - 1) return false;
+    const int K = P.K, C = P.C, R = 2 * K + 1, jp = j - 1;
+    // independent loads together: token, uniform and the partials
+    const int32_t x = P.tokens[(int64_t)b * K + jp];
+    const float u = greedy ? 0.f : P.uniforms[(int64_t)b * (K + 1) + jp];
+    const RowStat t = merge_row(P.part + ((int64_t)b * R + jp) * C, C, P.s, greedy);
+    RowStat d = {0.f, 0.f, 0, 0};
+    if (!greedy && P.draft != nullptr) d = merge_row(P.part + ((int64_t)b * R + K + 1 + jp) * C, C, P.s, false);
+    return !position_test<DTT, DTD>(P, b, jp, greedy, t, d, x, u).stop;
+}
+
+template <int DTT, int DTD>
+__global__ __launch_bounds__(NT) void k_rowstats_lazy(const Params P, const int j)
+{
+    const int K = P.K, R = 2 * K + 1;
+    const int Rj = j < K ? 2 : 1;
+    const int per_seq = Rj * P.C;
+    const int b = blockIdx.x / per_seq;
+    const int rem = blockIdx.x - b * per_seq;
+    const int r = rem / P.C;                       // 0: target row j, 1: draft row j
+    const int c = rem - r * P.C;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    __shared__ SmState sh_sm[NWAVE];
+    __shared__ AmState sh_am[NWAVE];
+    __shared__ int sh_go;
+
+    if (r == 1 && (greedy || P.draft == nullptr)) return;       // never read
+    if (threadIdx.x == 0) sh_go = reaches<DTT, DTD>(P, b, j, greedy) ? 1 : 0;
+    __syncthreads();
+    if (!sh_go) return;
+    if (threadIdx.x == 0 && r == 0 && c == 0) P.reach[b] = j;
+
+    const int64_t cl = chunk_len(P.V, P.C);
+    const int64_t e0 = (int64_t)c * cl;
+    const int64_t e1 = e0 + cl < (int64_t)P.V ? e0 + cl : (int64_t)P.V;
+    const int row = r == 0 ? j : K + 1 + j;
+    Partial* dst = P.part + ((int64_t)b * R + row) * P.C + c;
+    if (r == 1)
+        rowstats_body<DTD>(P, draft_row<DTD>(P, b, j), e0, e1, false, dst, sh_sm, sh_am);
+    else
+        rowstats_body<DTT>(P, target_row<DTT>(P, b, j), e0, e1, greedy, dst, sh_sm, sh_am);
 }
 
 // ----------------------------------------------------- draw: final token --
@@ -579,30 +680,37 @@ __device__ __forceinline__ float weight(float l, float d, float s, float cp, flo
     return fmaxf(0.f, __builtin_fmaf(-w, eq, ep));
 }
 
-// k_decide: one workgroup per (sequence b, tile t of the vocabulary).  Every
-// workgroup settles n itself (tile 0 also writes the outputs); sampling
-// sequences then sum the draw weights of row n over the tile's segments
-// (64*8 elements, one per wave iteration) into the workspace.
+// k_decide: one workgroup per sequence settles n and writes the outputs and
+// the record the draw launches read.
 template <int DTT, int DTD>
 __global__ __launch_bounds__(NT) void k_decide(const Params P)
 {
+    const int b = blockIdx.x;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    __shared__ Decision dec;
+    decide_seq<DTT, DTD>(P, b, greedy, true, &dec);
+}
+
+// k_tiles: one workgroup per (sampling sequence b, vocabulary tile t): the
+// draw weights of row n (residual max(0, p - q) scaled by Z_p, or p for the
+// bonus) summed per segment of 64*8 elements (one per wave iteration).
+template <int DTT, int DTD>
+__global__ __launch_bounds__(NT) void k_tiles(const Params P)
+{
     const int b = blockIdx.x / P.tiles;
     const int t = blockIdx.x - b * P.tiles;
-    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
-    if (greedy && t > 0) return;
-    __shared__ Decision dec;
-    decide_seq<DTT, DTD>(P, b, greedy, t == 0, &dec);
-    if (greedy || !dec.ok) return;                  // uniform: dec is shared
+    const SeqRec rec = P.rec[b];
+    if (rec.status != 1) return;                    // greedy, invalid: nothing to draw
 
     const int K = P.K, V = P.V, nseg = P.nseg;
     const float s = P.s;
-    const int n = dec.n;
+    const int n = rec.n;
     const bool bonus = n == K;
     const char* trow = target_row<DTT>(P, b, n);
     const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
-    const float cp = shift_of(dec.mp, s);
-    const float cq = bonus ? 0.f : shift_of(dec.mq, s);
-    const float w = bonus ? 0.f : dec.zp / dec.zq;
+    const float cp = shift_of(rec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
+    const float w = bonus ? 0.f : rec.zp / rec.zq;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
@@ -776,8 +884,36 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
 
 struct Plan {
     int C, nseg, tiles;
-    size_t off_rec, off_part, off_seg, total;
+    bool lazy;
+    size_t off_rec, off_reach, off_part, off_seg, total;
 };
+
+// 0 = choose per call, 1 = eager, 2 = lazy (sv_set_mode; SV_MODE in the environment)
+static std::atomic<int> g_mode{-1};
+
+static int mode_now()
+{
+    int m = g_mode.load(std::memory_order_relaxed);
+    if (m < 0) {
+        const char* e = getenv("SV_MODE");
+        m = (e && !strcmp(e, "eager")) ? 1 : (e && !strcmp(e, "lazy")) ? 2 : 0;
+        int expect = -1;
+        g_mode.compare_exchange_strong(expect, m);
+        m = g_mode.load(std::memory_order_relaxed);
+    }
+    return m;
+}
+
+// Lazy mode pays one launch per position; it wins once a call streams enough
+// bytes that skipping the unexamined rows outweighs K extra launches.
+static bool choose_lazy(int32_t B, int32_t K, int32_t V, int32_t dtt)
+{
+    const int m = mode_now();
+    if (m == 1 || K == 0) return false;
+    if (m == 2) return true;
+    const double bytes = (double)B * (K + 1) * V * (dtt == SV_BF16 ? 2 : 4);
+    return bytes >= 32.0 * (1 << 20);
+}
 
 static int env_int(const char* name, int dflt)
 {
@@ -790,25 +926,28 @@ static int env_int(const char* name, int dflt)
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static bool make_plan(int32_t B, int32_t K, int32_t V, Plan* pl)
+static bool make_plan(int32_t B, int32_t K, int32_t V, bool lazy, Plan* pl)
 {
     const int64_t R = 2 * (int64_t)K + 1;
     const int64_t rows = (int64_t)B * R;
+    const int64_t rows_per_launch = lazy ? (int64_t)B * 2 : rows;
     const int64_t n8 = ((int64_t)V + 7) / 8;
     int64_t max_c = n8 / ((int64_t)NT * UNROLL);        // at least one full window per lane
     if (max_c < 1) max_c = 1;
     static const int target_items = env_int("SV_TARGET_ITEMS", 4096);
     static const int forced_c = env_int("SV_CHUNKS", 0);
-    int64_t C = rows > 0 ? (target_items + rows - 1) / rows : 1;
+    int64_t C = rows_per_launch > 0 ? (target_items + rows_per_launch - 1) / rows_per_launch : 1;
     if (forced_c > 0) C = forced_c;
     if (C > max_c) C = max_c;
     if (C < 1) C = 1;
     pl->C = (int)C;
+    pl->lazy = lazy;
     pl->nseg = (int)(((int64_t)V + SEG - 1) / SEG);
     pl->tiles = (pl->nseg + SPT - 1) / SPT;
     if (rows * C > INT_MAX || (int64_t)B * pl->tiles > INT_MAX) return false;
     size_t o = 0;
     pl->off_rec = o;  o = align_up(o + sizeof(SeqRec) * (size_t)B, 256);
+    pl->off_reach = o; o = align_up(o + sizeof(int32_t) * (size_t)B, 256);
     pl->off_part = o; o = align_up(o + sizeof(Partial) * (size_t)(rows * C), 256);
     pl->off_seg = o;  o = align_up(o + sizeof(float) * 2 * (size_t)B * (size_t)pl->nseg, 256);
     pl->total = o;
@@ -844,7 +983,7 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
         for (const float* q : d)
             if (q && !aligned_to(q, 4)) return SV_EINVAL;
     }
-    if (!make_plan(B, K, V, pl)) return SV_EINVAL;
+    if (!make_plan(B, K, V, choose_lazy(B, K, V, dtt), pl)) return SV_EINVAL;
     if (!ws || !aligned_to(ws, 16) || ws_bytes < pl->total) return SV_EWORKSPACE;
     char* w = static_cast<char*>(ws);
     P->target = target;
@@ -860,6 +999,7 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->lse_q = diag ? diag->lse_q : nullptr;
     P->res_mass = diag ? diag->res_mass : nullptr;
     P->rec = reinterpret_cast<SeqRec*>(w + pl->off_rec);
+    P->reach = reinterpret_cast<int32_t*>(w + pl->off_reach);
     P->part = reinterpret_cast<Partial*>(w + pl->off_part);
     P->seg = reinterpret_cast<float*>(w + pl->off_seg);
     P->B = B;
@@ -875,14 +1015,22 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
 template <int DTT, int DTD>
 static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
 {
-    const dim3 grid((unsigned)((int64_t)P.B * (2 * P.K + 1) * pl.C));
-    hipLaunchKernelGGL((k_rowstats<DTT, DTD>), grid, dim3(NT), 0, st, P);
+    if (!pl.lazy) {
+        const dim3 grid((unsigned)((int64_t)P.B * (2 * P.K + 1) * pl.C));
+        hipLaunchKernelGGL((k_rowstats<DTT, DTD>), grid, dim3(NT), 0, st, P);
+        return;
+    }
+    for (int j = 0; j <= P.K; ++j) {
+        const dim3 grid((unsigned)((int64_t)P.B * (j < P.K ? 2 : 1) * pl.C));
+        hipLaunchKernelGGL((k_rowstats_lazy<DTT, DTD>), grid, dim3(NT), 0, st, P, j);
+    }
 }
 
 template <int DTT, int DTD>
 static void launch_draw_t(const Params& P, const Plan& pl, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_decide<DTT, DTD>), dim3((unsigned)((int64_t)P.B * pl.tiles)), dim3(NT), 0, st, P);
+    hipLaunchKernelGGL((k_decide<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
+    hipLaunchKernelGGL((k_tiles<DTT, DTD>), dim3((unsigned)((int64_t)P.B * pl.tiles)), dim3(NT), 0, st, P);
     hipLaunchKernelGGL((k_search<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
 }
 
@@ -936,9 +1084,9 @@ extern "C" {
 size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
 {
     if (B <= 0 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(dtype)) return 0;
-    sv::Plan pl;
-    if (!sv::make_plan(B, K, V, &pl)) return 0;
-    return pl.total;
+    sv::Plan pe, pz;
+    if (!sv::make_plan(B, K, V, false, &pe) || !sv::make_plan(B, K, V, true, &pz)) return 0;
+    return pe.total > pz.total ? pe.total : pz.total;
 }
 
 #define SV_ARGS_DECL                                                                           \
@@ -986,6 +1134,15 @@ int sv_draw(SV_ARGS_DECL)
     SV_PREPARE;
     return sv::launch_draw(P, pl, dtype, dtype, st);
 }
+
+int sv_set_mode(int mode)
+{
+    if (mode < 0 || mode > 2) return SV_EINVAL;
+    sv::g_mode.store(mode, std::memory_order_relaxed);
+    return SV_OK;
+}
+
+int sv_get_mode(void) { return sv::mode_now(); }
 
 const char* sv_strerror(int code)
 {

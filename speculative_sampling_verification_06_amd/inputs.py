@@ -286,3 +286,24 @@ def needed_bytes(w: Workload, accepted_len: np.ndarray) -> int:
             tot += (2 if n < K else 1) * V * s
     return tot
 
+
+
+def reached_bytes(w: Workload, accepted_len: np.ndarray) -> int:
+    """Bytes of logits the row statistics read when only reached positions are
+    streamed: (n+1) target rows, plus min(n+1, K) draft rows for sampling
+    sequences.  Invalid sequences (n = -1) count their first position only."""
+    s = w.elem_bytes
+    V, K = w.V, w.K
+    tot = 0
+    for b, n in enumerate(np.asarray(accepted_len).tolist()):
+        m = max(n, 0)
+        tot += (m + 1) * V * s
+        if not w.greedy[b]:
+            tot += min(m + 1, K) * V * s
+    return tot
+
+
+def lazy_schedule(w: Workload) -> bool:
+    """Whether the library's automatic schedule streams positions lazily for
+    this shape (one eager pass would read at least 32 MiB)."""
+    return w.K > 0 and w.B * (w.K + 1) * w.V * w.elem_bytes >= 32 * (1 << 20)

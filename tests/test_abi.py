@@ -139,3 +139,21 @@ def test_fused_verify_checks_everything_before_launch(lib, kw):
                                 a["tokens"], a["uniforms"], C.c_float(a["T"]), a["greedy"], a["B"], a["K"],
                                 a["V"], a["acc"], a["out"], a["diag"], a["ws"], a["ws_bytes"], None)
     assert rc in (binding.SV_EINVAL, binding.SV_EWORKSPACE)
+
+
+def test_mode_knob(lib):
+    assert lib.sv_set_mode(3) == binding.SV_EINVAL and lib.sv_set_mode(-1) == binding.SV_EINVAL
+    old = lib.sv_get_mode()
+    for m in (binding.MODE_EAGER, binding.MODE_LAZY, binding.MODE_AUTO):
+        assert lib.sv_set_mode(m) == binding.SV_OK and lib.sv_get_mode() == m
+    lib.sv_set_mode(old)
+
+
+def test_workspace_covers_both_schedules(lib):
+    # one workspace must serve either schedule for the same shape
+    a = binding.workspace_bytes(256, 8, 152064, binding.SV_BF16)
+    old = lib.sv_get_mode()
+    for m in (binding.MODE_EAGER, binding.MODE_LAZY):
+        lib.sv_set_mode(m)
+        assert binding.workspace_bytes(256, 8, 152064, binding.SV_BF16) == a
+    lib.sv_set_mode(old)

@@ -224,3 +224,69 @@ def test_gpu_output_law_chi_square(dev):
     pv = S._checks(w, p, q, acc, toks)
     _log(f"[parity] gpu chi-square p-values {pv}")
     assert min(pv.values()) > S.ALPHA, pv
+
+
+# ---------------------------------------------------------------------------
+# Both row-statistics schedules (eager: every row; lazy: one launch per
+# position, rows past the first rejection never read) against the oracle.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def schedule(dev, request):
+    binding.set_mode(request.param)
+    yield request.param
+    binding.set_mode(binding.MODE_AUTO)
+
+
+SCHED = pytest.mark.parametrize("schedule", [binding.MODE_EAGER, binding.MODE_LAZY],
+                                indirect=True, ids=["eager", "lazy"])
+
+
+@SCHED
+@pytest.mark.parametrize("make", [lambda: I.tiny(), lambda: I.tiny(greedy=True), lambda: I.cfg_32k(),
+                                  lambda: I.cfg_128k(), lambda: I.cfg_152k()],
+                         ids=["tiny", "tiny_greedy", "32k", "128k", "152k"])
+def test_schedules_named_workloads(dev, schedule, make):
+    check(make(), dev)
+
+
+@SCHED
+@pytest.mark.parametrize("B,K,V,dtype,greedy_every,sd", [
+    (5, 3, 4097, I.BF16, 2, 0.3), (3, 2, 1001, I.F32, 0, 3.0), (2, 63, 300, I.F32, 2, 0.2),
+    (33, 6, 20000, I.BF16, 0, 0.5), (16, 8, 70001, I.BF16, 3, 0.1)])
+def test_schedules_ragged(dev, schedule, B, K, V, dtype, greedy_every, sd):
+    mask = np.zeros(B, np.uint8) if not greedy_every else (np.arange(B) % greedy_every == 0).astype(np.uint8)
+    w = I.synth_logits(77 + B + K, B, K, V, dtype=dtype, T=0.9, sigma=3.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=sd, greedy_mask=mask, name=f"sched_{B}_{K}_{V}")
+    check(w, dev)
+
+
+@SCHED
+def test_schedules_invalid_inputs(dev, schedule):
+    test_masked_tokens_and_invalid_inputs(dev)
+
+
+@SCHED
+def test_schedules_deterministic_and_split(dev, schedule):
+    test_deterministic_and_split_launches(dev)
+
+
+def test_lazy_reads_only_reached_rows(dev):
+    """A NaN planted in a row after the first rejection is never read in lazy
+    mode (the eager stream reads it but the method ignores it; both agree)."""
+    import torch
+    w = I.cfg_152k(B=16)
+    o = oracle.verify(w)
+    t = w.target.copy()
+    for b in range(w.B):
+        n = int(o.accepted_len[b])
+        if n + 1 <= w.K:
+            t[b, n + 1:, :] = 0x7FC0
+    w2 = I.Workload(w.name, w.B, w.K, w.V, w.dtype, w.T, t, w.draft, w.tokens, w.uniforms, w.greedy)
+    for m in (binding.MODE_EAGER, binding.MODE_LAZY):
+        binding.set_mode(m)
+        try:
+            g = run_gpu(w2, dev)
+        finally:
+            binding.set_mode(binding.MODE_AUTO)
+        parity.compare(w2, g, o)
