@@ -176,7 +176,8 @@ int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* t
 
 /* Row-statistics schedule, process-wide (thread-safe; a tuning knob, it never
  * changes a decision):
- *   SV_MODE_AUTO  per call: lazy when one eager pass would stream >= 32 MiB
+ *   SV_MODE_AUTO  per call: lazy when one eager pass would stream at least
+ *                 64 MiB of logits per position (K+1 launches then pay off)
  *   SV_MODE_EAGER one launch streams every row of every position
  *   SV_MODE_LAZY  one launch per position streams it only for sequences that
  *                 reach it (rows past the first rejection are never read)

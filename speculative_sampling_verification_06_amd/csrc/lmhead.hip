@@ -15,8 +15,10 @@
 // waves; each wave owns 64 vocabulary rows of Wt (two 32-wide MFMA tiles) and
 // all 192 hidden rows (six 32-row tiles) of an M block, so every Wt element
 // is read from HBM exactly once and each 16-k step issues 12
-// v_mfma_f32_32x32x16_bf16.  Wt fragments are prefetched PF steps ahead in
-// registers; hidden fragments (1.5 MB, L2-resident) one step ahead.
+// v_mfma_f32_32x32x16_bf16.  Wt fragments stream into a register ring two
+// 64-k blocks deep; the hidden states (1.5 MB, L2-resident) come through a
+// double-buffered LDS block shared by the four waves, the next block's loads
+// in flight while the current one is multiplied.
 // Accumulation is fp32; bf16 x bf16 products are exact in fp32.
 //
 // MFMA 32x32x16 operand layout (lane l, 8 bf16 per operand):
@@ -42,7 +44,6 @@ constexpr int WN = 64;            // vocabulary rows per wave
 constexpr int BN = 4 * WN;        // per workgroup
 constexpr int MT = 6;             // 32-row tiles per M block
 constexpr int MB = 32 * MT;       // 192 hidden rows per M block
-constexpr int PF = 4;             // Wt prefetch depth, in 16-k steps
 
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p)
 {
@@ -68,33 +69,74 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, ui
     }
 }
 
-__global__ __launch_bounds__(NT) void k_lmhead(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wt,
-                                               float* __restrict__ out, int M, int d, int V)
+// Hidden-state block of BK k-columns for all MB rows, staged in LDS and
+// shared by the four waves.  Rows are padded to A_LD bf16 (144 bytes) so the
+// 16 lanes of each ds_read_b128 group hit all 64 banks once.
+constexpr int BK = 64;                 // k per LDS block
+constexpr int KS = BK / 16;            // MFMA k-steps per block
+constexpr int A_LD = BK + 8;           // padded LDS row stride, bf16
+constexpr int A_PIECES = MB * BK / 8;  // 16-byte pieces per block
+constexpr int A_PER_T = A_PIECES / NT; // per thread (6)
+constexpr int WPF = 2 * KS;            // Wt prefetch depth in k-steps (two blocks)
+static_assert(A_PIECES % NT == 0, "block pieces must split evenly");
+
+__global__ __launch_bounds__(NT, 1) void k_lmhead(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wt,
+                                                  float* __restrict__ out, int M, int d, int V)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][MB * A_LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, kg = lane >> 5;
     const int n0 = blockIdx.x * BN + wave * WN;
     const int m0 = blockIdx.y * MB;
     const int nsteps = (d + 15) / 16;
+    const int nblk = (d + BK - 1) / BK;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    const bf16x8 zero = {};
 
-    // rows past M or V read the last valid row; their results are not stored
+    // rows past V read the last valid row; their results are not stored
     const uint16_t* bp[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int v = min(n0 + 32 * c + li, V - 1);
         bp[c] = Wt + (int64_t)v * d + 8 * kg;
     }
-    const uint16_t* ap[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int m = min(m0 + 32 * t + li, M - 1);
-        ap[t] = H + (int64_t)m * d + 8 * kg;
-    }
-    const bf16x8 zero = {};
-    // k slots past d (d % 16 == 8) are zero
-    auto ldk = [&](const uint16_t* p, int step) -> bf16x8 {
-        return (step * 16 + 8 * kg < d) ? ld16(p + step * 16) : zero;
+    auto ldw = [&](int c, int step) -> bf16x8 {
+        return (step < nsteps && step * 16 + 8 * kg < d) ? ld16(bp[c] + step * 16) : zero;
     };
+    // this thread's share of a hidden-state block: pieces tid + i*NT, i < 6,
+    // held in six named registers (an indexable array would be moved to LDS)
+    static_assert(A_PER_T == 6, "staging below is written out for six pieces");
+    const int ar = tid >> 3, ac = (tid & 7) * 8;               // piece i: row ar + 32*i
+#define LM_SRC(i) (H + (int64_t)min(m0 + ar + 32 * (i), M - 1) * d + ac)
+    const uint16_t* hs0 = LM_SRC(0);
+    const uint16_t* hs1 = LM_SRC(1);
+    const uint16_t* hs2 = LM_SRC(2);
+    const uint16_t* hs3 = LM_SRC(3);
+    const uint16_t* hs4 = LM_SRC(4);
+    const uint16_t* hs5 = LM_SRC(5);
+#undef LM_SRC
+    uint4 s0, s1, s2, s3, s4, s5;
+#define LM_LOAD_A(kb)                                                                          \
+    do {                                                                                       \
+        const bool ok_ = (kb) < nblk && (kb) * BK + ac < d;                                   \
+        const int64_t o_ = (int64_t)(kb) * BK;                                                \
+        s0 = ok_ ? *reinterpret_cast<const uint4*>(hs0 + o_) : z4;                             \
+        s1 = ok_ ? *reinterpret_cast<const uint4*>(hs1 + o_) : z4;                             \
+        s2 = ok_ ? *reinterpret_cast<const uint4*>(hs2 + o_) : z4;                             \
+        s3 = ok_ ? *reinterpret_cast<const uint4*>(hs3 + o_) : z4;                             \
+        s4 = ok_ ? *reinterpret_cast<const uint4*>(hs4 + o_) : z4;                             \
+        s5 = ok_ ? *reinterpret_cast<const uint4*>(hs5 + o_) : z4;                             \
+    } while (0)
+#define LM_STORE_A(buf)                                                                        \
+    do {                                                                                       \
+        uint16_t* a_ = &As[buf][ar * A_LD + ac];                                              \
+        *reinterpret_cast<uint4*>(a_ + 0 * 32 * A_LD) = s0;                                   \
+        *reinterpret_cast<uint4*>(a_ + 1 * 32 * A_LD) = s1;                                   \
+        *reinterpret_cast<uint4*>(a_ + 2 * 32 * A_LD) = s2;                                   \
+        *reinterpret_cast<uint4*>(a_ + 3 * 32 * A_LD) = s3;                                   \
+        *reinterpret_cast<uint4*>(a_ + 4 * 32 * A_LD) = s4;                                   \
+        *reinterpret_cast<uint4*>(a_ + 5 * 32 * A_LD) = s5;                                   \
+    } while (0)
 
     f32x16 acc[MT][2];
 #pragma unroll
@@ -102,42 +144,51 @@ __global__ __launch_bounds__(NT) void k_lmhead(const uint16_t* __restrict__ H, c
         acc[t][0] = f32x16{};
         acc[t][1] = f32x16{};
     }
-    bf16x8 wb[PF][2];
+    bf16x8 wb[WPF][2];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        wb[p][0] = p < nsteps ? ldk(bp[0], p) : zero;
-        wb[p][1] = p < nsteps ? ldk(bp[1], p) : zero;
+    for (int q = 0; q < WPF; ++q) {
+        wb[q][0] = ldw(0, q);
+        wb[q][1] = ldw(1, q);
     }
-    bf16x8 an[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) an[t] = ldk(ap[t], 0);
+    LM_LOAD_A(0);
+    LM_STORE_A(0);
+    LM_LOAD_A(1);
+    __syncthreads();
 
-    for (int i0 = 0; i0 < nsteps; i0 += PF) {
+    // blocks in pairs so every Wt ring slot index is a compile-time constant
+    for (int kb0 = 0; kb0 < nblk; kb0 += 2) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int i = i0 + p;
-            if (i < nsteps) {
-                const bf16x8 b0 = wb[p][0], b1 = wb[p][1];
-                bf16x8 a[MT];
+        for (int h = 0; h < 2; ++h) {
+            const int kb = kb0 + h;
+            if (kb < nblk) {
+                const uint16_t* as = As[h] + li * A_LD + 8 * kg;
 #pragma unroll
-                for (int t = 0; t < MT; ++t) a[t] = an[t];
-                if (i + PF < nsteps) {
-                    wb[p][0] = ldk(bp[0], i + PF);
-                    wb[p][1] = ldk(bp[1], i + PF);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int step = kb * KS + ks;
+                    const int slot = h * KS + ks;
+                    const bf16x8 b0 = wb[slot][0], b1 = wb[slot][1];
+                    wb[slot][0] = ldw(0, step + WPF);
+                    wb[slot][1] = ldw(1, step + WPF);
+                    if (step < nsteps) {
+#pragma unroll
+                        for (int t = 0; t < MT; ++t) {
+                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + t * 32 * A_LD + ks * 16);
+                            acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[t][0], 0, 0, 0);
+                            acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[t][1], 0, 0, 0);
+                        }
+                    }
                 }
-                if (i + 1 < nsteps) {
-#pragma unroll
-                    for (int t = 0; t < MT; ++t) an[t] = ldk(ap[t], i + 1);
-                }
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], b0, acc[t][0], 0, 0, 0);
-                    acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], b1, acc[t][1], 0, 0, 0);
-                }
+                // block kb+1 (in registers) into the other buffer; every wave
+                // finished reading that buffer before the previous barrier
+                LM_STORE_A(h ^ 1);
+                __syncthreads();
+                LM_LOAD_A(kb + 2);
             }
         }
     }
 
+#undef LM_LOAD_A
+#undef LM_STORE_A
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll

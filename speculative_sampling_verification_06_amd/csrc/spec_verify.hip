@@ -904,15 +904,16 @@ static int mode_now()
     return m;
 }
 
-// Lazy mode pays one launch per position; it wins once a call streams enough
-// bytes that skipping the unexamined rows outweighs K extra launches.
-static bool choose_lazy(int32_t B, int32_t K, int32_t V, int32_t dtt)
+// Lazy mode pays one latency-bound launch per position (5-20 us each on
+// gfx950); it wins once the eager stream is long against K+1 such launches:
+// at least 64 MiB of logits per position.
+static bool choose_lazy(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd)
 {
     const int m = mode_now();
     if (m == 1 || K == 0) return false;
     if (m == 2) return true;
-    const double bytes = (double)B * (K + 1) * V * (dtt == SV_BF16 ? 2 : 4);
-    return bytes >= 32.0 * (1 << 20);
+    const double bytes = (double)B * V * ((double)(K + 1) * (dtt == SV_BF16 ? 2 : 4) + (double)K * (dtd == SV_BF16 ? 2 : 4));
+    return bytes >= (double)(K + 1) * 64.0 * (1 << 20);
 }
 
 static int env_int(const char* name, int dflt)
@@ -983,7 +984,7 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
         for (const float* q : d)
             if (q && !aligned_to(q, 4)) return SV_EINVAL;
     }
-    if (!make_plan(B, K, V, choose_lazy(B, K, V, dtt), pl)) return SV_EINVAL;
+    if (!make_plan(B, K, V, choose_lazy(B, K, V, dtt, dtd), pl)) return SV_EINVAL;
     if (!ws || !aligned_to(ws, 16) || ws_bytes < pl->total) return SV_EWORKSPACE;
     char* w = static_cast<char*>(ws);
     P->target = target;
