@@ -174,6 +174,44 @@ int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* t
                        int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
                        const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- draft-side sampling step ---------------------------------------------
+ * Each draft pass draws its candidate x ~ q = softmax(d / T) ([QH] "Một vòng":
+ * the drafter proposes its candidates one pass at a time; [MC]'s sketch
+ * samples from draft.probs).  sv_sample draws one token per row of
+ * logits [B, V] (dtype SV_F32 / SV_BF16) with uniforms [B] in [0, 1) by the
+ * same inverse CDF as the final draw (ascending token index); greedy rows
+ * (greedy_flag[b] = 1; NULL = none) take the lowest-index argmax.  Outputs
+ * tokens [B] (-1 for an invalid row: NaN / +Inf / all -Inf logits or a
+ * uniform outside [0, 1)) and optionally lse [B] = ln sum_i exp(d_i / T)
+ * (NaN for greedy rows).  It is the verify step with K = 0 and shares its
+ * kernels; workspace from sv_sample_workspace_bytes.  Errors as spec_verify. */
+size_t sv_sample_workspace_bytes(int32_t B, int32_t V, int32_t dtype);
+int sv_sample(const void* logits, int32_t dtype, const float* uniforms, float temperature,
+              const uint8_t* greedy_flag, int32_t B, int32_t V, int32_t* tokens, float* lse,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- KV-cache commit ---------------------------------------------------------
+ * After verification only the accepted prefix may become committed decoding
+ * state ([NL] "Verifikasi mengubah jalur cache": truncation, staged writes or
+ * index management).  Caches are P planes (e.g. keys and values of every
+ * layer) of B sequences of l_max rows of row_bytes bytes:
+ *   cache  [P, B, l_max, row_bytes]    cache_len [B] int32 (in: committed
+ *   length before the round; out: after)
+ *   staged [P, B, K + offset, row_bytes]: the entries the pass computed for
+ *   its inputs; offset = 1 when they start with the previous round's final
+ *   token, 0 when they hold the K candidates only.
+ * With c_b = accepted_len[b] + offset, rows staged[:, b, 0:c_b] are copied to
+ * cache[:, b, len_b : len_b + c_b] and len_b grows by c_b.  staged == NULL
+ * means the pass wrote the entries in place at [len_b, len_b + K + offset):
+ * committing is then the length update alone.  accepted_len[b] = -1 or a
+ * commit that would pass l_max leaves sequence b unchanged; status [B]
+ * (optional) gets 0 committed, 1 invalid, 2 would overflow.  Works for the
+ * draft model's cache the same way.  EINVAL on P < 1, K out of range, offset
+ * not 0/1, l_max < 1, row_bytes < 1, NULL or misaligned (4 B) int arrays. */
+int sv_kv_commit(void* cache, int32_t* cache_len, const void* staged, const int32_t* accepted_len,
+                 int32_t planes, int32_t B, int32_t K, int32_t offset, int64_t l_max, int64_t row_bytes,
+                 int32_t* status, void* stream);
+
 /* Row-statistics schedule, process-wide (thread-safe; a tuning knob, it never
  * changes a decision):
  *   SV_MODE_AUTO  per call: lazy when one eager pass would stream at least

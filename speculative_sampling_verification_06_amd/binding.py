@@ -22,7 +22,9 @@ SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
-           "spec_lmhead_verify", "sv_set_mode", "sv_get_mode", "sv_strerror", "sv_version")
+           "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
+           "sv_set_mode", "sv_get_mode",
+           "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY = 0, 1, 2
 
 
@@ -66,6 +68,14 @@ def load_library(path: str = LIB_PATH):
             lib.sv_strerror.argtypes = [C.c_int]
             lib.sv_version.restype = C.c_int
             lib.sv_version.argtypes = []
+            lib.sv_sample_workspace_bytes.restype = C.c_size_t
+            lib.sv_sample_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+            lib.sv_sample.restype = C.c_int
+            lib.sv_sample.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_float, C.c_void_p, C.c_int32,
+                                      C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+            lib.sv_kv_commit.restype = C.c_int
+            lib.sv_kv_commit.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
             lib.sv_set_mode.restype = C.c_int
             lib.sv_set_mode.argtypes = [C.c_int]
             lib.sv_get_mode.restype = C.c_int
@@ -417,3 +427,80 @@ def bf16_tensor(bits, device):
     torch = _torch()
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+# ------------------------------------------------------- draft-side sampling --
+
+def sample(logits, uniforms, temperature, greedy=None, *, lse=False, stream=None):
+    """x ~ softmax(logits / T) per row of logits [B, V] (argmax for greedy rows).
+
+    Returns tokens [B] int32 (-1 for an invalid row), and lse [B] if asked."""
+    torch = _torch()
+    lib = load_library()
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    dt = _dtype_code(logits)
+    dev = logits.device
+    _dev_ptr(logits, "logits", shape=(B, V))
+    _dev_ptr(uniforms, "uniforms", torch.float32, (B,))
+    if greedy is not None:
+        _dev_ptr(greedy, "greedy_flag", torch.uint8, (B,))
+    tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    out_lse = torch.empty(B, dtype=torch.float32, device=dev) if lse else None
+    need = lib.sv_sample_workspace_bytes(B, V, dt)
+    ws = get_workspace(need, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check_rc(lib.sv_sample(logits.data_ptr() if B else None, dt, uniforms.data_ptr() if B else None,
+                            C.c_float(float(temperature)), None if greedy is None else greedy.data_ptr(), B, V,
+                            tokens.data_ptr() if B else None, None if out_lse is None else out_lse.data_ptr(),
+                            ws.data_ptr(), ws.numel(), stream))
+    return (tokens, out_lse) if lse else tokens
+
+
+# --------------------------------------------------------------- KV commit --
+
+def kv_commit(cache, cache_len, staged, accepted_len, offset=1, status=None, stream=None):
+    """Commit the accepted prefix: cache [P, B, L, ...], cache_len [B] int32 (updated in place),
+    staged [P, B, K + offset, ...] (or None: entries already written in place),
+    accepted_len [B] int32.  The trailing dims of cache and staged are one row (any dtype).
+    Returns status [B] int32 (0 committed, 1 invalid, 2 would overflow)."""
+    torch = _torch()
+    P, B, L = cache.shape[:3]
+    row_bytes = cache[0, 0, 0].numel() * cache.element_size() if L else 0
+    _dev_ptr(cache, "cache")
+    _dev_ptr(cache_len, "cache_len", torch.int32, (B,))
+    _dev_ptr(accepted_len, "accepted_len", torch.int32, (B,))
+    if staged is not None:
+        _dev_ptr(staged, "staged")
+        if staged.shape[0] != P or staged.shape[1] != B or staged.dtype != cache.dtype or \
+                staged[0, 0, 0].numel() * staged.element_size() != row_bytes:
+            raise ValueError("staged must be [P, B, K + offset, row] like the cache")
+        K = staged.shape[2] - offset
+    else:
+        raise ValueError("give K through staged, or use kv_commit_in_place")
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=cache.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(cache.device).cuda_stream
+    _check_rc(load_library().sv_kv_commit(cache.data_ptr(), cache_len.data_ptr(), staged.data_ptr(),
+                                          accepted_len.data_ptr(), P, B, K, offset, L, row_bytes,
+                                          status.data_ptr(), stream))
+    return status
+
+
+def kv_commit_in_place(cache_len, accepted_len, K, offset=1, l_max=None, status=None, stream=None):
+    """The in-place variant: entries already sit at [len, len + K + offset); only lengths change."""
+    torch = _torch()
+    B = cache_len.shape[0]
+    _dev_ptr(cache_len, "cache_len", torch.int32, (B,))
+    _dev_ptr(accepted_len, "accepted_len", torch.int32, (B,))
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=cache_len.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(cache_len.device).cuda_stream
+    _check_rc(load_library().sv_kv_commit(None, cache_len.data_ptr(), None, accepted_len.data_ptr(), 1, B, K,
+                                          offset, int(l_max if l_max is not None else 2 ** 62), 1,
+                                          status.data_ptr(), stream))
+    return status

@@ -1136,6 +1136,28 @@ int sv_draw(SV_ARGS_DECL)
     return sv::launch_draw(P, pl, dtype, dtype, st);
 }
 
+size_t sv_sample_workspace_bytes(int32_t B, int32_t V, int32_t dtype)
+{
+    const size_t w = sv_workspace_bytes(B, 0, V, dtype);
+    return w ? w + sv::align_up(sizeof(int32_t) * (size_t)B, 256) : 0;
+}
+
+int sv_sample(const void* logits, int32_t dtype, const float* uniforms, float temperature,
+              const uint8_t* greedy_flag, int32_t B, int32_t V, int32_t* tokens, float* lse,
+              void* workspace, size_t workspace_bytes, void* stream)
+{
+    // the verify step with K = 0: no tests, the final draw from p_0
+    if (B < 0 || V < 1) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    const size_t w0 = sv_workspace_bytes(B, 0, V, dtype);
+    if (w0 == 0) return SV_EINVAL;
+    if (!workspace || workspace_bytes < sv_sample_workspace_bytes(B, V, dtype)) return SV_EWORKSPACE;
+    int32_t* acc = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w0);
+    sv_diag dg = {nullptr, nullptr, lse, nullptr, nullptr};
+    return sv_verify_mixed(logits, nullptr, nullptr, uniforms, temperature, greedy_flag, B, 0, V, dtype, dtype,
+                           acc, tokens, lse ? &dg : nullptr, workspace, w0, stream, 0);
+}
+
 int sv_set_mode(int mode)
 {
     if (mode < 0 || mode > 2) return SV_EINVAL;
