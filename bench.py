@@ -199,12 +199,94 @@ def bench_lmhead(args, torch, np, binding, I, dev):
     return w, gpu, res, "lmhead"
 
 
+def _timed_one(torch, stream, K, fn):
+    import numpy as np
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / K, np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
+
+
+def bench_sample(args, torch, np, binding, I, dev):
+    """Draft-side sampling step: one token per row of [256, 152064] bf16 logits."""
+    w = I.synth_logits(1003, 256, 0, 152064, dtype=I.BF16, T=1.0, sigma=4.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=2.5, name="sample_B256_V152064_bf16")
+    d = binding.to_device(w, dev)
+    logits = d["target"][:, 0, :].contiguous()
+    u = d["uniforms"][:, 0].contiguous()
+    call = binding.BoundSample(logits, u, w.T)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        call()
+    ms, ev = _timed_one(torch, stream, args.steps, call)
+    tok = call().cpu().numpy()
+    bytes_ = w.B * w.V * 2 + w.B * w.V * 2            # every row once, then the drawn row once more
+    res = _base_result(w, args.steps, args.warmup, ms, "f32")
+    res["metric"] = "draft-step sampled logits/s (B·V per sec), 1 GPU"
+    res["value"] = w.B * w.V / (ms * 1e-3)
+    res["config"] = {"workload": w.name, "B": w.B, "V": w.V, "logits": "bf16", "temperature": w.T, "seed": w.seed}
+    achieved = bytes_ / (float(ev.mean()) * 1e-3) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "sv_sample (all launches)",
+                       "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": float(ev.mean())}
+    g = {"accepted_len": np.where(tok >= 0, 0, -1).astype(np.int32), "out_tokens": tok[:, None]}
+    return w, g, res, "sample"
+
+
+def bench_kvcommit(args, torch, np, binding, I, dev):
+    """KV-cache commit: 64 planes (32 layers x keys/values) of 2048-byte rows
+    (8 heads x 128 x bf16), B=256, K=8, staging block = previous final token +
+    8 candidates, L=512; accepted lengths follow the 152k-vocab workload."""
+    P, B, K, L, row = 64, 256, 8, 512, 2048
+    rng = np.random.default_rng(7)
+    hist = np.array([185, 57, 9, 5, 0, 0, 0, 0, 0], np.float64)
+    acc = rng.choice(K + 1, size=B, p=hist / hist.sum()).astype(np.int32)
+    cache = torch.empty(P, B, L, row, dtype=torch.uint8, device=dev)
+    staged = torch.randint(0, 255, (P, B, K + 1, row), dtype=torch.uint8, device=dev)
+    ln0 = torch.from_numpy(rng.integers(0, L - K - 2, size=B).astype(np.int32)).to(dev)
+    ln = ln0.clone()
+    acc_d = torch.from_numpy(acc).to(dev)
+    call = binding.BoundKvCommit(cache, ln, staged, acc_d, 1)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ln.copy_(ln0)          # same starting lengths every step
+        call()
+    for _ in range(args.warmup):
+        step()
+    ms, ev = _timed_one(torch, stream, args.steps, step)
+    committed = int((acc + 1).sum()) * P * row
+    bytes_ = 2 * committed                              # read staged rows, write cache rows
+
+    class _W:
+        name, B_, verified_logits = f"kvcommit_P{P}_B{B}_K{K}_row{row}", B, 0
+    res = _base_result(_W, args.steps, args.warmup, ms, "u8")
+    res["metric"] = "committed KV bytes/s, 1 GPU"
+    res["value"] = committed / (ms * 1e-3)
+    res["unit"] = "B/s"
+    res["config"] = {"workload": _W.name, "planes": P, "B": B, "K": K, "L": L, "row_bytes": row,
+                     "committed_bytes_per_step": committed}
+    achieved = bytes_ / (float(ev.mean()) * 1e-3) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                       "kernel": "k_kv_copy + k_kv_len (+ a length reset copy)",
+                       "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": float(ev.mean())}
+    return None, None, res, "kv"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="cfg152k", choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead"])
+    ap.add_argument("--config", default="cfg152k",
+                    choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead", "sample", "kvcommit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing (repeated whole-workload calls)")
@@ -234,10 +316,12 @@ def main() -> int:
     binding.load_library()
     binding.set_mode({"auto": binding.MODE_AUTO, "eager": binding.MODE_EAGER, "lazy": binding.MODE_LAZY}[args.mode])
 
-    fn = bench_lmhead if args.config == "lmhead" else bench_verify
+    fn = {"lmhead": bench_lmhead, "sample": bench_sample, "kvcommit": bench_kvcommit}.get(args.config, bench_verify)
     w, gpu, result, kind = fn(args, torch, np, binding, I, dev)
 
-    if not args.no_cpu_baseline:
+    if kind == "kv":
+        result["cpu_baseline"] = None
+    elif not args.no_cpu_baseline:
         import oracle
         from oracle import parity
         oracle.build(force=False)

@@ -504,3 +504,51 @@ def kv_commit_in_place(cache_len, accepted_len, K, offset=1, l_max=None, status=
                                           offset, int(l_max if l_max is not None else 2 ** 62), 1,
                                           status.data_ptr(), stream))
     return status
+
+
+
+class BoundSample:
+    """sv_sample on fixed tensors with pre-marshalled arguments."""
+
+    def __init__(self, logits, uniforms, temperature, greedy=None, stream=None):
+        torch = _torch()
+        self.tokens = sample(logits, uniforms, temperature, greedy)       # checked once
+        B, V = logits.shape
+        dt = _dtype_code(logits)
+        lib = load_library()
+        ws = get_workspace(lib.sv_sample_workspace_bytes(B, V, dt), logits.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(logits.device).cuda_stream
+        self._keep = (logits, uniforms, greedy, ws)
+        self._fn = lib.sv_sample
+        self._args = (C.c_void_p(logits.data_ptr()), C.c_int32(dt), C.c_void_p(uniforms.data_ptr()),
+                      C.c_float(float(temperature)), C.c_void_p(None if greedy is None else greedy.data_ptr()),
+                      C.c_int32(B), C.c_int32(V), C.c_void_p(self.tokens.data_ptr()), None,
+                      C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel()), C.c_void_p(stream))
+
+    def __call__(self):
+        _check_rc(self._fn(*self._args))
+        return self.tokens
+
+
+class BoundKvCommit:
+    """sv_kv_commit on fixed tensors with pre-marshalled arguments."""
+
+    def __init__(self, cache, cache_len, staged, accepted_len, offset=1, stream=None):
+        torch = _torch()
+        P, B, L = cache.shape[:3]
+        row_bytes = cache[0, 0, 0].numel() * cache.element_size()
+        K = staged.shape[2] - offset
+        self.status = torch.empty(B, dtype=torch.int32, device=cache.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(cache.device).cuda_stream
+        self._keep = (cache, cache_len, staged, accepted_len)
+        self._fn = load_library().sv_kv_commit
+        self._args = (C.c_void_p(cache.data_ptr()), C.c_void_p(cache_len.data_ptr()), C.c_void_p(staged.data_ptr()),
+                      C.c_void_p(accepted_len.data_ptr()), C.c_int32(P), C.c_int32(B), C.c_int32(K),
+                      C.c_int32(offset), C.c_int64(L), C.c_int64(row_bytes), C.c_void_p(self.status.data_ptr()),
+                      C.c_void_p(stream))
+
+    def __call__(self):
+        _check_rc(self._fn(*self._args))
+        return self.status
