@@ -104,6 +104,11 @@ def _method_stats(w, acc):
             "page_context": "pages quote 2-3x end-to-end decode speed-up, no hardware stated"}
 
 
+SCHEDULES = {1: "eager (one launch streams every row)",
+             2: "lazy (one launch per position, reached rows only)",
+             3: "seq (one workgroup per sequence walks its positions, reached rows only, draws in place)"}
+
+
 def bench_verify(args, torch, np, binding, I, dev):
     w = I.CONFIGS[args.config]()
     print(f"[bench] workload {w.name}: generated", file=sys.stderr, flush=True)
@@ -129,20 +134,29 @@ def bench_verify(args, torch, np, binding, I, dev):
     eager = I.eager_bytes(w)
     acc = out["accepted_len"].cpu().numpy()
     gpu = {k: v.cpu().numpy() for k, v in out.items()}
-    mode = binding.get_mode()
-    lazy = mode == binding.MODE_LAZY or (mode == binding.MODE_AUTO and I.lazy_schedule(w))
-    stats_bytes = I.reached_bytes(w, acc) if lazy else eager
+    sched = binding.schedule(w.B, w.K, w.V, w.dtype)
+    lazy = sched == binding.MODE_LAZY
+    seq = sched == binding.MODE_SEQ
+    # eager: every row once; lazy: the rows reached; seq: the whole step in one
+    # launch, so the rows reached plus the draw's second pass over row n
+    stats_bytes = I.needed_bytes(w, acc) if seq else (I.reached_bytes(w, acc) if lazy else eager)
     achieved = stats_bytes / (float(stats_ms.mean()) * 1e-3) / 1e9
     step_ev = stats_ms + draw_ms
     res = _base_result(w, args.steps, args.warmup, ms, "f32")
     res["config"] = {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "logits": I.DTYPE_NAMES[w.dtype],
                      "temperature": w.T, "greedy_sequences": int(w.greedy.sum()), "seed": w.seed,
                      "verified_logits_per_step": w.verified_logits,
-                     "schedule": "lazy (one launch per position, reached rows only)" if lazy else "eager"}
+                     "schedule": SCHEDULES[sched]}
+    if seq:
+        res["config"]["workgroups_per_sequence"] = binding.seq_groups(w.B, w.K, w.V, w.dtype)
+    kname = {binding.MODE_EAGER: "k_rowstats", binding.MODE_LAZY: "k_rowstats_lazy",
+             binding.MODE_SEQ: "k_seqg" if seq and binding.seq_groups(w.B, w.K, w.V, w.dtype) > 1 else "k_seq"}[sched]
     res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": achieved / HBM_PEAK_GBS,
-                       "traffic": _traffic("k_rowstats_lazy" if lazy else "k_rowstats", w.name, "spec_verify.hip"),
-                       "kernel": "k_rowstats_lazy (all K+1 launches of a step)" if lazy else "k_rowstats",
+                       "traffic": _traffic(kname, w.name, "spec_verify.hip"),
+                       "kernel": {binding.MODE_EAGER: "k_rowstats",
+                                  binding.MODE_LAZY: "k_rowstats_lazy (all K+1 launches of a step)",
+                                  binding.MODE_SEQ: "k_seq/k_seqg (the whole step, draw included)"}[sched],
                        "algorithmic_bytes_per_launch": stats_bytes,
                        "avg_launch_ms": float(stats_ms.mean())}
     res["timing_ms"] = {"step_events_median": float(np.median(step_ev)),
@@ -230,7 +244,8 @@ def bench_sample(args, torch, np, binding, I, dev):
     res = _base_result(w, args.steps, args.warmup, ms, "f32")
     res["metric"] = "draft-step sampled logits/s (B·V per sec), 1 GPU"
     res["value"] = w.B * w.V / (ms * 1e-3)
-    res["config"] = {"workload": w.name, "B": w.B, "V": w.V, "logits": "bf16", "temperature": w.T, "seed": w.seed}
+    res["config"] = {"workload": w.name, "B": w.B, "V": w.V, "logits": "bf16", "temperature": w.T, "seed": w.seed,
+                     "schedule": SCHEDULES[binding.schedule(w.B, 0, w.V, w.dtype)]}
     achieved = bytes_ / (float(ev.mean()) * 1e-3) / 1e9
     res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "sv_sample (all launches)",
@@ -290,8 +305,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing (repeated whole-workload calls)")
-    ap.add_argument("--mode", choices=["auto", "eager", "lazy"], default="auto",
+    ap.add_argument("--mode", choices=["auto", "eager", "lazy", "seq"], default="auto",
                     help="row-statistics schedule (the library chooses per call under auto)")
+    ap.add_argument("--seq-groups", type=int, default=0,
+                    help="cap on workgroups per sequence under --mode seq (0: as many as the device holds)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this size (for PMC byte scaling)")
     args = ap.parse_args()
@@ -314,7 +331,9 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     binding.load_library()
-    binding.set_mode({"auto": binding.MODE_AUTO, "eager": binding.MODE_EAGER, "lazy": binding.MODE_LAZY}[args.mode])
+    binding.set_mode({"auto": binding.MODE_AUTO, "eager": binding.MODE_EAGER, "lazy": binding.MODE_LAZY,
+                      "seq": binding.MODE_SEQ}[args.mode])
+    binding.set_seq_groups(args.seq_groups)
 
     fn = {"lmhead": bench_lmhead, "sample": bench_sample, "kvcommit": bench_kvcommit}.get(args.config, bench_verify)
     w, gpu, result, kind = fn(args, torch, np, binding, I, dev)

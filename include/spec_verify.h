@@ -127,11 +127,12 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* The same call in two parts, for timing and for checking the parts against
- * the whole: sv_stats streams every target row, and the draft rows of
- * sampling sequences, once into per-chunk
- * statistics (the HBM-bound part); sv_draw settles n, writes the outputs and
- * makes the final draw of sampling sequences.  sv_draw must follow sv_stats
- * on the same stream with identical arguments.                              */
+ * the whole: sv_stats streams the target rows, and the draft rows of
+ * sampling sequences, once into per-chunk statistics (the HBM-bound part);
+ * sv_draw settles n, writes the outputs and makes the final draw of sampling
+ * sequences.  sv_draw must follow sv_stats on the same stream with identical
+ * arguments and the same schedule (sv_set_mode).  Under SV_MODE_SEQ the
+ * whole step runs in sv_stats and sv_draw launches nothing.                 */
 int sv_stats(const void* target_logits, const void* draft_logits,
              const int32_t* draft_tokens, const float* uniforms,
              float temperature, const uint8_t* greedy_flag,
@@ -212,20 +213,43 @@ int sv_kv_commit(void* cache, int32_t* cache_len, const void* staged, const int3
                  int32_t planes, int32_t B, int32_t K, int32_t offset, int64_t l_max, int64_t row_bytes,
                  int32_t* status, void* stream);
 
-/* Row-statistics schedule, process-wide (thread-safe; a tuning knob, it never
- * changes a decision):
- *   SV_MODE_AUTO  per call: lazy when one eager pass would stream at least
- *                 64 MiB of logits per position (K+1 launches then pay off)
+/* Row-statistics schedule, process-wide (thread-safe; a tuning knob: every
+ * schedule meets the same definition, though float sums taken in another
+ * order may settle a draw within rounding of a boundary differently):
+ *   SV_MODE_AUTO  per call: SV_MODE_SEQ when position 0 alone streams at
+ *                 least 64 MiB (and the vocabulary fits its limit), else lazy
+ *                 when one eager pass would stream at least 64 MiB of logits
+ *                 per position (K+1 launches then pay off), else eager
  *   SV_MODE_EAGER one launch streams every row of every position
  *   SV_MODE_LAZY  one launch per position streams it only for sequences that
  *                 reach it (rows past the first rejection are never read)
- * The environment variable SV_MODE=eager|lazy sets the initial value.
+ *   SV_MODE_SEQ   one launch, one workgroup per sequence walking its own
+ *                 positions up to the first rejection and drawing at the end;
+ *                 vocabularies above 2,097,152 entries use SV_MODE_LAZY
+ * The environment variable SV_MODE=eager|lazy|seq sets the initial value.
  * sv_set_mode returns SV_EINVAL for other values.                          */
 #define SV_MODE_AUTO  0
 #define SV_MODE_EAGER 1
 #define SV_MODE_LAZY  2
+#define SV_MODE_SEQ   3
 int sv_set_mode(int mode);
 int sv_get_mode(void);
+
+/* The schedule (SV_MODE_EAGER, SV_MODE_LAZY or SV_MODE_SEQ) a verify call of
+ * this shape and these storage types would use under the current mode;
+ * SV_EINVAL for a shape or type the call would reject.                     */
+int sv_schedule(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
+
+/* Under SV_MODE_SEQ each sequence gets G workgroups that split every row it
+ * reaches and exchange partial statistics through the workspace (tagged
+ * words; nothing to initialise), G as large as the device holds all of them
+ * at once; G = 1 is one 1024-thread workgroup per sequence.
+ * sv_set_seq_groups caps G (1..64; 0 = no cap, the default; the environment
+ * variable SV_SEQ_GROUPS sets the initial cap); SV_EINVAL otherwise.
+ * sv_seq_groups: the G a call of this shape would use now (0 when it would
+ * not run SV_MODE_SEQ), SV_EINVAL for a shape the call would reject.       */
+int sv_set_seq_groups(int groups);
+int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
 
 /* Short text for a return code (static storage). */
 const char* sv_strerror(int code);

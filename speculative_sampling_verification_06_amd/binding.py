@@ -23,9 +23,9 @@ SV_MAX_K = 63
 # The exported names, as declared in include/spec_verify.h.
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
-           "sv_set_mode", "sv_get_mode",
+           "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups",
            "sv_strerror", "sv_version")
-MODE_AUTO, MODE_EAGER, MODE_LAZY = 0, 1, 2
+MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
 
 
 class SvDiag(C.Structure):
@@ -80,6 +80,12 @@ def load_library(path: str = LIB_PATH):
             lib.sv_set_mode.argtypes = [C.c_int]
             lib.sv_get_mode.restype = C.c_int
             lib.sv_get_mode.argtypes = []
+            lib.sv_schedule.restype = C.c_int
+            lib.sv_schedule.argtypes = [C.c_int32] * 5
+            lib.sv_set_seq_groups.restype = C.c_int
+            lib.sv_set_seq_groups.argtypes = [C.c_int]
+            lib.sv_seq_groups.restype = C.c_int
+            lib.sv_seq_groups.argtypes = [C.c_int32] * 5
             lib.sv_lmhead_pack.restype = C.c_int
             lib.sv_lmhead_pack.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
             lib.sv_lmhead.restype = C.c_int
@@ -103,7 +109,7 @@ def workspace_bytes(B: int, K: int, V: int, dtype: int) -> int:
 
 
 def set_mode(mode: int) -> None:
-    """Row-statistics schedule for later calls: MODE_AUTO, MODE_EAGER or MODE_LAZY."""
+    """Row-statistics schedule for later calls: MODE_AUTO, MODE_EAGER, MODE_LAZY or MODE_SEQ."""
     rc = load_library().sv_set_mode(int(mode))
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
@@ -111,6 +117,30 @@ def set_mode(mode: int) -> None:
 
 def get_mode() -> int:
     return int(load_library().sv_get_mode())
+
+
+def set_seq_groups(groups: int) -> None:
+    """Cap on workgroups per sequence under MODE_SEQ (0 = as many as the device holds)."""
+    rc = load_library().sv_set_seq_groups(int(groups))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+
+
+def seq_groups(B: int, K: int, V: int, target_dtype: int, draft_dtype=None) -> int:
+    """Workgroups per sequence a MODE_SEQ call of this shape would use (0: not MODE_SEQ)."""
+    rc = int(load_library().sv_seq_groups(B, K, V, target_dtype,
+                                          target_dtype if draft_dtype is None else draft_dtype))
+    if rc < 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return rc
+
+
+def schedule(B: int, K: int, V: int, target_dtype: int, draft_dtype=None) -> int:
+    """MODE_EAGER, MODE_LAZY or MODE_SEQ: what a verify call of this shape would run."""
+    rc = int(load_library().sv_schedule(B, K, V, target_dtype, target_dtype if draft_dtype is None else draft_dtype))
+    if rc < 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return rc
 
 
 # ------------------------------------------------------------------ torch --

@@ -105,8 +105,12 @@ struct Params {
     SeqRec* rec;
     int32_t* reach;   // lazy mode: last position each sequence was seen alive at
     float* seg;       // [2][B][nseg]: residual sums, then p sums
+    uint64_t* slots;  // grouped per-sequence schedule: tagged words the G workgroups of a sequence exchange
+    uint32_t* gep;    // grouped schedule: per-sequence call counter (tags)
     int32_t B, K, V, C;
     int32_t nseg, tiles;
+    int32_t G, gsegs; // grouped schedule: workgroups per sequence, segments per workgroup slice
+    uint32_t salt;    // grouped schedule: shape hash folded into the tags
     float s;          // log2(e) / T
 };
 
@@ -248,32 +252,33 @@ __device__ __forceinline__ void am_window(const float* x, IdxF idx, AmState& st)
     }
 }
 
-// Stream elements [e0, e1) of one row (e0 a multiple of E) into the state.
-template <int DT, bool GREEDY>
+// Stream elements [e0, e1) of one row (e0 a multiple of E) into the state;
+// BT threads, U 16-byte loads in flight per lane.
+template <int DT, bool GREEDY, int BT = NT, int U = UNROLL>
 __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t e1, float s,
                                            SmState& sm, AmState& am)
 {
     constexpr int E = Fmt<DT>::E;
-    constexpr int W = UNROLL * E;
+    constexpr int W = U * E;
     const int tid = threadIdx.x;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     if (aligned) {
         const uint4* vrow = reinterpret_cast<const uint4*>(row);
         const int64_t v0 = e0 / E, v1 = e1 / E;
-        for (int64_t base = v0 + tid; base < v1; base += (int64_t)NT * UNROLL) {
-            uint4 raw[UNROLL];
+        for (int64_t base = v0 + tid; base < v1; base += (int64_t)BT * U) {
+            uint4 raw[U];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int64_t vi = base + (int64_t)u * NT;
+            for (int u = 0; u < U; ++u) {
+                const int64_t vi = base + (int64_t)u * BT;
                 if (vi < v1) raw[u] = vrow[vi];
                 else raw[u] = make_uint4(Fmt<DT>::NEG_INF_WORD, Fmt<DT>::NEG_INF_WORD,
                                          Fmt<DT>::NEG_INF_WORD, Fmt<DT>::NEG_INF_WORD);
             }
             float x[W];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) unpack<DT>(raw[u], x + u * E);
+            for (int u = 0; u < U; ++u) unpack<DT>(raw[u], x + u * E);
             if constexpr (GREEDY)
-                am_window<W>(x, [base](int k) { return (base + (int64_t)(k / E) * NT) * E + (k % E); }, am);
+                am_window<W>(x, [base](int k) { return (base + (int64_t)(k / E) * BT) * E + (k % E); }, am);
             else
                 sm_window<W>(x, s, sm);
         }
@@ -285,15 +290,15 @@ __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t 
             else sm_window<1>(x1, s, sm);
         }
     } else {
-        for (int64_t base = e0 + tid; base < e1; base += (int64_t)NT * W) {
+        for (int64_t base = e0 + tid; base < e1; base += (int64_t)BT * W) {
             float x[W];
 #pragma unroll
             for (int k = 0; k < W; ++k) {
-                const int64_t i = base + (int64_t)k * NT;
+                const int64_t i = base + (int64_t)k * BT;
                 x[k] = (i < e1) ? load1<DT>(row, i) : NEG_INF;
             }
             if constexpr (GREEDY)
-                am_window<W>(x, [base](int k) { return base + (int64_t)k * NT; }, am);
+                am_window<W>(x, [base](int k) { return base + (int64_t)k * BT; }, am);
             else
                 sm_window<W>(x, s, sm);
         }
@@ -302,36 +307,53 @@ __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t 
 
 // ------------------------------------------------------- block reductions --
 
-__device__ __forceinline__ SmState block_reduce_sm(SmState v, float s, SmState* sh)
+// Butterfly over the wave; lane 0 holds the reduction in a fixed order.
+__device__ __forceinline__ SmState wave_reduce_sm(SmState v, float s)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         SmState o = {__shfl_xor(v.m, off, 64), __shfl_xor(v.z, off, 64)};
         v = sm_merge(v, o, s);
     }
-    if (lane == 0) sh[wave] = v;
-    __syncthreads();
-    SmState r = sh[0];
-#pragma unroll
-    for (int w = 1; w < NWAVE; ++w) r = sm_merge(r, sh[w], s);
-    return r;
+    return v;
 }
 
-__device__ __forceinline__ AmState block_reduce_am(AmState v, AmState* sh)
+__device__ __forceinline__ AmState wave_reduce_am(AmState v)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         AmState o = {__shfl_xor(v.v, off, 64), __shfl_xor(v.i, off, 64),
                      (uint32_t)__shfl_xor((int)v.bad, off, 64)};
         v = am_merge(v, o);
     }
+    return v;
+}
+
+// Workgroup of BT threads; sh holds BT/64 states.  Every thread returns the
+// waves' states merged in wave order.
+template <int BT = NT>
+__device__ __forceinline__ SmState block_reduce_sm(SmState v, float s, SmState* sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_reduce_sm(v, s);
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    SmState r = sh[0];
+#pragma unroll
+    for (int w = 1; w < BT / 64; ++w) r = sm_merge(r, sh[w], s);
+    return r;
+}
+
+template <int BT = NT>
+__device__ __forceinline__ AmState block_reduce_am(AmState v, AmState* sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_reduce_am(v);
     if (lane == 0) sh[wave] = v;
     __syncthreads();
     AmState r = sh[0];
 #pragma unroll
-    for (int w = 1; w < NWAVE; ++w) r = am_merge(r, sh[w]);
+    for (int w = 1; w < BT / 64; ++w) r = am_merge(r, sh[w]);
     return r;
 }
 
@@ -353,7 +375,9 @@ __device__ __forceinline__ float wave_incl_scan(float v)
     return v;
 }
 
-// Inclusive scan over the workgroup; *total gets the sum of all NT values.
+// Inclusive scan over a workgroup of BT threads; *total gets the sum of all
+// BT values.  sh holds BT/64 floats.
+template <int BT = NT>
 __device__ __forceinline__ float block_incl_scan(float v, float* sh, float* total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -362,7 +386,7 @@ __device__ __forceinline__ float block_incl_scan(float v, float* sh, float* tota
     __syncthreads();
     float off = 0.f, tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
+    for (int w = 0; w < BT / 64; ++w) {
         if (w < wave) off += sh[w];
         tot += sh[w];
     }
@@ -445,22 +469,25 @@ struct Decision {
     float mp, zp, mq, zq, u;
 };
 
-// Merge the sequence's chunk partials (fixed chunk order), run the K tests on
-// wave 0 and find the first rejection with one ballot.  Called by every
-// workgroup that needs n; all of them reach the same result bit for bit.  With
-// write_out, also writes accepted_len, the accepted prefix, the greedy token,
-// the diagnostics and the record the search launch reads.  Every thread of the
-// workgroup must call it; *dec is valid for all threads on return.
-// Merged statistics of one row from its C chunk partials, always in chunk
-// order (every caller gets the same bits).
+// Merged statistics of one row.
 struct RowStat {
     float m, z;       // softmax: running max and sum; greedy: max value (z unused)
     int32_t i;        // greedy: lowest index of the max
     int32_t ok;       // row valid
 };
 
+__device__ __forceinline__ RowStat rowstat_am(const AmState& am)
+{
+    return {am.v, 0.f, am.i, (am.bad == 0u) && am.v > NEG_INF && am.v < POS_INF};
+}
+
+__device__ __forceinline__ RowStat rowstat_sm(const SmState& sm)
+{
+    return {sm.m, sm.z, 0, (sm.z > 0.f) && (sm.z < POS_INF) && sm.m > NEG_INF && sm.m < POS_INF};
+}
+
 // Partials are loaded eight at a time (independent loads, one round trip)
-// and merged in chunk order.
+// and merged in chunk order, so every caller gets the same bits.
 constexpr int MERGE_BATCH = 8;
 
 __device__ __forceinline__ RowStat merge_row(const Partial* pp, int C, float s, bool greedy)
@@ -480,8 +507,7 @@ __device__ __forceinline__ RowStat merge_row(const Partial* pp, int C, float s, 
             }
         }
     }
-    if (greedy) return {am.v, 0.f, am.i, (am.bad == 0u) && am.v > NEG_INF && am.v < POS_INF};
-    return {sm.m, sm.z, 0, (sm.z > 0.f) && (sm.z < POS_INF) && sm.m > NEG_INF && sm.m < POS_INF};
+    return greedy ? rowstat_am(am) : rowstat_sm(sm);
 }
 
 struct TestOut {
@@ -489,16 +515,23 @@ struct TestOut {
     float ptok, qtok;
 };
 
+// What the test at position j reads besides the row statistics: the draft
+// token x, its uniform u, and the target and draft logits at x.  For j = K
+// only u (the draw's uniform) is meaningful.
+struct TestIn {
+    int32_t x;
+    float u, lx, dx;
+};
+
 // The test at position j (j < K): greedy keeps x_j iff it is the lowest-index
 // argmax of target row j; sampling keeps it iff u_j * q_j(x_j) < p_j(x_j).
-// stop = rejected or invalid.  t, d: merged target row j and draft row j.
-template <int DTT, int DTD>
-__device__ __forceinline__ TestOut position_test(const Params& P, int b, int j, bool greedy, const RowStat& t,
-                                                 const RowStat& d, int32_t x, float u)
+// stop = rejected or invalid.  t, d: merged target row j and draft row j; lx
+// and dx are read only when the test is valid.
+__device__ __forceinline__ TestOut test_from(int V, float s, bool greedy, const RowStat& t, const RowStat& d,
+                                             int32_t x, float u, float lx, float dx)
 {
-    const float s = P.s;
     TestOut o = {true, true, NAN, NAN};
-    const bool tok_ok = x >= 0 && x < P.V;
+    const bool tok_ok = x >= 0 && x < V;
     if (greedy) {
         o.inval = !(t.ok && tok_ok);
         o.stop = o.inval || x != t.i;
@@ -507,8 +540,6 @@ __device__ __forceinline__ TestOut position_test(const Params& P, int b, int j, 
     const bool u_ok = u >= 0.f && u < 1.f;
     o.inval = !(t.ok && d.ok && tok_ok && u_ok);
     if (o.inval) return o;
-    const float lx = load1<DTT>(target_row<DTT>(P, b, j), x);
-    const float dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
     o.ptok = ex2(__builtin_fmaf(lx, s, -shift_of(t.m, s))) / t.z;
     o.qtok = ex2(__builtin_fmaf(dx, s, -shift_of(d.m, s))) / d.z;
     o.stop = !(u * o.qtok < o.ptok);
@@ -516,20 +547,52 @@ __device__ __forceinline__ TestOut position_test(const Params& P, int b, int j, 
 }
 
 template <int DTT, int DTD>
-__device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, Decision* dec)
+__device__ __forceinline__ TestOut position_test(const Params& P, int b, int j, bool greedy, const RowStat& t,
+                                                 const RowStat& d, int32_t x, float u)
 {
-    const int K = P.K, C = P.C, R = 2 * K + 1;
+    float lx = 0.f, dx = 0.f;
+    if (!greedy && t.ok && d.ok && x >= 0 && x < P.V && u >= 0.f && u < 1.f) {
+        lx = load1<DTT>(target_row<DTT>(P, b, j), x);
+        dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
+    }
+    return test_from(P.V, P.s, greedy, t, d, x, u, lx, dx);
+}
+
+// Test inputs of position j <= K, loaded before the row statistics exist (the
+// logits at x are read whenever x is in range).
+template <int DTT, int DTD>
+__device__ __forceinline__ TestIn load_test_in(const Params& P, int b, int j, bool greedy)
+{
+    const int K = P.K;
+    TestIn r = {-1, 0.f, 0.f, 0.f};
+    if (!greedy) r.u = P.uniforms[(int64_t)b * (K + 1) + j];
+    if (j < K) {
+        r.x = P.tokens[(int64_t)b * K + j];
+        if (!greedy && r.x >= 0 && r.x < P.V) {
+            r.lx = load1<DTT>(target_row<DTT>(P, b, j), r.x);
+            if (P.draft) r.dx = load1<DTD>(draft_row<DTD>(P, b, j), r.x);
+        }
+    }
+    return r;
+}
+
+// Runs the K tests on wave 0 from the merged row statistics f_rs (target rows
+// 0..K, then draft rows 0..K-1) and finds the first rejection n with one
+// ballot; every workgroup that needs n reaches the same result bit for bit.
+// Rows past the first rejection may hold anything: only examined positions
+// matter.  ti: test inputs already loaded (K+1 entries), or null to load them
+// here.  With write_out, also writes accepted_len, the accepted prefix, the
+// greedy token, the diagnostics and the record the search launch reads;
+// draw_here leaves out_tokens[b, n] and res_mass of a sampling sequence to a
+// draw in the same workgroup.  Every thread must call it; *dec is valid for
+// all threads on return.
+template <int DTT, int DTD>
+__device__ void decide_core(const Params& P, int b, bool greedy, bool write_out, bool draw_here,
+                            const RowStat* f_rs, const TestIn* ti, Decision* dec)
+{
+    const int K = P.K;
     const float s = P.s;
     const int tid = threadIdx.x;
-    __shared__ RowStat f_rs[MAXR];
-
-    if (tid < R) {
-        const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
-        const bool draft_row_ = tid > K;
-        if (draft_row_ && (greedy || P.draft == nullptr)) f_rs[tid] = {0.f, 0.f, 0, 0};
-        else f_rs[tid] = merge_row(pp, C, s, greedy);
-    }
-    __syncthreads();
 
     if (tid < 64) {
         const int j = tid;
@@ -538,9 +601,15 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         float ptok = NAN, qtok = NAN;
         int32_t x = -1;
         if (j < K) {
-            x = P.tokens[(int64_t)b * K + j];
-            const float u = greedy ? 0.f : P.uniforms[ub + j];
-            const TestOut o = position_test<DTT, DTD>(P, b, j, greedy, f_rs[j], f_rs[K + 1 + j], x, u);
+            TestOut o;
+            if (ti) {
+                x = ti[j].x;
+                o = test_from(P.V, s, greedy, f_rs[j], f_rs[K + 1 + j], x, ti[j].u, ti[j].lx, ti[j].dx);
+            } else {
+                x = P.tokens[(int64_t)b * K + j];
+                const float u = greedy ? 0.f : P.uniforms[ub + j];
+                o = position_test<DTT, DTD>(P, b, j, greedy, f_rs[j], f_rs[K + 1 + j], x, u);
+            }
             stop = o.stop;
             inval = o.inval;
             ptok = o.ptok;
@@ -553,7 +622,7 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         float uK = 0.f;
         if (!bad && n == K) bad = !f_rs[K].ok;
         if (!bad && !greedy) {
-            uK = P.uniforms[ub + K];
+            uK = ti ? ti[K].u : P.uniforms[ub + K];
             bad = !(uK >= 0.f && uK < 1.f);
         }
         if (j == 0) {
@@ -580,7 +649,8 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
                     put(P.res_mass, b, NAN);
                 }
             } else {
-                if (j <= K) out[j] = (j < n) ? x : ((j == n && greedy) ? f_rs[n].i : -1);
+                const bool drawn_later = draw_here && !greedy && j == n;
+                if (j <= K && !drawn_later) out[j] = (j < n) ? x : ((j == n && greedy) ? f_rs[n].i : -1);
                 const bool seen = !greedy && j <= n;
                 if (j < K) {
                     put(P.p_tok, (int64_t)b * K + j, seen ? ptok : NAN);
@@ -594,7 +664,7 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
                     if (greedy) put(P.res_mass, b, 0.f);
                 }
             }
-            if (j == 0) {
+            if (j == 0 && !draw_here) {
                 SeqRec r;
                 r.n = n;
                 r.status = (!bad && !greedy) ? 1 : 0;
@@ -609,6 +679,24 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         }
     }
     __syncthreads();
+}
+
+// Merges the sequence's chunk partials into row statistics, then decides.
+template <int DTT, int DTD>
+__device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, Decision* dec)
+{
+    const int K = P.K, C = P.C, R = 2 * K + 1;
+    const int tid = threadIdx.x;
+    __shared__ RowStat f_rs[MAXR];
+
+    if (tid < R) {
+        const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
+        const bool draft_row_ = tid > K;
+        if (draft_row_ && (greedy || P.draft == nullptr)) f_rs[tid] = {0.f, 0.f, 0, 0};
+        else f_rs[tid] = merge_row(pp, C, P.s, greedy);
+    }
+    __syncthreads();
+    decide_core<DTT, DTD>(P, b, greedy, write_out, false, f_rs, nullptr, dec);
 }
 
 // --------------------------- k_rowstats_lazy: position j, live rows only --
@@ -742,73 +830,45 @@ __global__ __launch_bounds__(NT) void k_tiles(const Params P)
     }
 }
 
-// k_search: one workgroup per sequence.  Scans the segment sums for the one
-// segment holding u*S, then walks that segment lane by lane.
-template <int DTT, int DTD>
-__global__ __launch_bounds__(NT) void k_search(const Params P)
+// Where the draw lands: the segment g holding u*S and the weight before it.
+struct Pick {
+    int mode;         // 0 residual, 1 bonus row p, 2 p fallback (residual rounded to nothing)
+    int g;            // segment, -1 if no segment has positive weight
+    bool overrun;     // rounding put u*S past the total: last positive weight
+    float S, thr, lo;
+};
+
+struct Locate {
+    int g;            // segment, -1 if none has positive weight
+    bool overrun;     // no running sum exceeded thr: g is the last positive segment
+    float lo;         // running sum before g
+};
+
+// First segment with positive weight whose running sum exceeds thr (chunked
+// block scans of BT values, the order the totals are taken in); only
+// segments with positive weight can hit, so rounding in the tree prefix never
+// picks an empty one.  Without a hit: the last segment with positive weight.
+// sh_scan and sh_seg hold BT/64 entries.  The sums may sit in global memory
+// or LDS.
+template <int BT>
+__device__ Locate locate_segment(const float* sums, int nseg, float thr, float* sh_scan, int* sh_seg, float* sh_lo)
 {
-    const int b = blockIdx.x;
-    const SeqRec rec = P.rec[b];
-    if (rec.status != 1) return;
-    const int K = P.K, V = P.V, nseg = P.nseg;
-    const float s = P.s;
-    const int n = rec.n;
-    const bool bonus = n == K;
-    const char* trow = target_row<DTT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
-    const float cp = shift_of(rec.mp, s);
-    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
-    const float w = bonus ? 0.f : rec.zp / rec.zq;
+    constexpr int NW = BT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ float sh_scan[NWAVE];
-    __shared__ int sh_seg[NWAVE];
-    __shared__ float sh_lo[NWAVE];
-    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
-    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
-
-    const float* sums_r = P.seg + (int64_t)b * nseg;
-    const float* sums_p = P.seg + ((int64_t)P.B + b) * nseg;
-
-    // total weight, in the chunked scan order the search uses
-    float S = 0.f;
-    for (int base = 0; base < nseg; base += NT) {
-        const float v = (base + tid < nseg) ? sums_r[base + tid] : 0.f;
-        float tot;
-        block_incl_scan(v, sh_scan, &tot);
-        S += tot;
-    }
-    int mode = bonus ? 1 : 0;
-    const float* sums = sums_r;
-    if (!(S > 0.f)) {                              // residual rounded to nothing: draw from p_n
-        mode = 2;
-        sums = sums_p;
-        S = 0.f;
-        for (int base = 0; base < nseg; base += NT) {
-            const float v = (base + tid < nseg) ? sums[base + tid] : 0.f;
-            float tot;
-            block_incl_scan(v, sh_scan, &tot);
-            S += tot;
-        }
-    }
-    const float thr = rec.u * S;
-
-    // first segment whose running sum exceeds thr.  Only segments with
-    // positive weight can hit, so rounding in the tree prefix never picks an
-    // empty one.
     int g = -1;
     float lo = 0.f;
     float off = 0.f;
-    for (int base = 0; base < nseg; base += NT) {
+    for (int base = 0; base < nseg; base += BT) {
         const float v = (base + tid < nseg) ? sums[base + tid] : 0.f;
         float tot;
-        const float incl = block_incl_scan(v, sh_scan, &tot);
+        const float incl = block_incl_scan<BT>(v, sh_scan, &tot);
         const bool hit = (base + tid < nseg) && v > 0.f && (off + incl > thr);
         const uint64_t m = __ballot(hit);
         if (lane == 0) sh_seg[wave] = m ? base + wave * 64 + (__ffsll((unsigned long long)m) - 1) : INT_MAX;
         __syncthreads();
         int best = INT_MAX;
 #pragma unroll
-        for (int w2 = 0; w2 < NWAVE; ++w2) best = min(best, sh_seg[w2]);
+        for (int w2 = 0; w2 < NW; ++w2) best = min(best, sh_seg[w2]);
         if (best != INT_MAX) {                    // uniform across the workgroup
             if (base + tid == best) sh_lo[0] = off + (incl - v);
             __syncthreads();
@@ -821,82 +881,746 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
     }
     const bool overrun = g < 0;
     if (overrun) {
-        // rounding overrun: the last segment with positive weight
-        for (int base = ((nseg - 1) / NT) * NT; base >= 0 && g < 0; base -= NT) {
+        for (int base = ((nseg - 1) / BT) * BT; base >= 0 && g < 0; base -= BT) {
             const bool pos = (base + tid < nseg) && sums[base + tid] > 0.f;
             const uint64_t m = __ballot(pos);
             if (lane == 0) sh_seg[wave] = m ? base + wave * 64 + (63 - __clzll((long long)m)) : -1;
             __syncthreads();
             int bestl = -1;
 #pragma unroll
-            for (int w2 = 0; w2 < NWAVE; ++w2) bestl = max(bestl, sh_seg[w2]);
+            for (int w2 = 0; w2 < NW; ++w2) bestl = max(bestl, sh_seg[w2]);
             g = bestl;
             __syncthreads();
         }
     }
+    return {g, overrun, lo};
+}
 
-    // one segment on wave 0: lane exclusive prefix, then an in-lane walk.
-    // Only a positive weight can be chosen; a segment with a positive sum
-    // always holds one.
-    if (wave == 0 && g >= 0) {
-        const int64_t e = (int64_t)g * SEG + (int64_t)lane * LE;
-        float xl[LE], xd[LE], wv[LE];
-        load8<DTT>(trow, e, V, t_al, xl);
-        if (mode == 0) load8<DTD>(drow, e, V, d_al, xd);
-        float ls = 0.f;
-#pragma unroll
-        for (int k = 0; k < LE; ++k) {
-            wv[k] = weight(xl[k], mode == 0 ? xd[k] : 0.f, s, cp, cq, w, mode);
-            ls += wv[k];
+// Total weight of the segment sums: residual sums_r, or p sums sums_p when
+// the residual rounded to nothing; then the segment holding u*S.
+template <int BT>
+__device__ Pick find_segment(const float* sums_r, const float* sums_p, int nseg, float u, bool bonus,
+                             float* sh_scan, int* sh_seg, float* sh_lo)
+{
+    const int tid = threadIdx.x;
+    Pick pk;
+    float S = 0.f;
+    for (int base = 0; base < nseg; base += BT) {
+        const float v = (base + tid < nseg) ? sums_r[base + tid] : 0.f;
+        float tot;
+        block_incl_scan<BT>(v, sh_scan, &tot);
+        S += tot;
+    }
+    pk.mode = bonus ? 1 : 0;
+    const float* sums = sums_r;
+    if (!(S > 0.f)) {                              // residual rounded to nothing: draw from p_n
+        pk.mode = 2;
+        sums = sums_p;
+        S = 0.f;
+        for (int base = 0; base < nseg; base += BT) {
+            const float v = (base + tid < nseg) ? sums[base + tid] : 0.f;
+            float tot;
+            block_incl_scan<BT>(v, sh_scan, &tot);
+            S += tot;
         }
-        const float incl = wave_incl_scan(ls);
-        const float thr2 = thr - lo;
-        float run = incl - ls;
-        int cand = -1;
+    }
+    const float thr = u * S;
+    const Locate L = locate_segment<BT>(sums, nseg, thr, sh_scan, sh_seg, sh_lo);
+    pk.g = L.g;
+    pk.overrun = L.overrun;
+    pk.S = S;
+    pk.thr = thr;
+    pk.lo = L.lo;
+    return pk;
+}
+
+// One segment on one wave: lane exclusive prefix, then an in-lane walk.  Only
+// a positive weight can be chosen; a segment with a positive sum always holds
+// one.  Returns the drawn index on every lane.
+template <int DTT, int DTD>
+__device__ int walk_segment(const char* trow, const char* drow, int V, const Pick& pk, float s, float cp,
+                            float cq, float w)
+{
+    const int lane = threadIdx.x & 63;
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+    const int g = pk.g, mode = pk.mode;
+    const int64_t e = (int64_t)g * SEG + (int64_t)lane * LE;
+    float xl[LE], xd[LE], wv[LE];
+    load8<DTT>(trow, e, V, t_al, xl);
+    if (mode == 0) load8<DTD>(drow, e, V, d_al, xd);
+    float ls = 0.f;
 #pragma unroll
-        for (int k = 0; k < LE; ++k) {
-            run += wv[k];
-            if (cand < 0 && wv[k] > 0.f && run > thr2) cand = k;
+    for (int k = 0; k < LE; ++k) {
+        wv[k] = weight(xl[k], mode == 0 ? xd[k] : 0.f, s, cp, cq, w, mode);
+        ls += wv[k];
+    }
+    const float incl = wave_incl_scan(ls);
+    const float thr2 = pk.thr - pk.lo;
+    float run = incl - ls;
+    int cand = -1;
+#pragma unroll
+    for (int k = 0; k < LE; ++k) {
+        run += wv[k];
+        if (cand < 0 && wv[k] > 0.f && run > thr2) cand = k;
+    }
+    const uint64_t m = pk.overrun ? 0ull : __ballot(cand >= 0);
+    if (m) {
+        const int L = __ffsll((unsigned long long)m) - 1;
+        return (int)((int64_t)g * SEG + (int64_t)L * LE + __shfl(cand, L, 64));
+    }
+    int lastk = -1;
+#pragma unroll
+    for (int k = 0; k < LE; ++k)
+        if (wv[k] > 0.f) lastk = k;
+    const uint64_t mp = __ballot(lastk >= 0);
+    const int L = mp ? 63 - __clzll((long long)mp) : 0;
+    const int kk = __shfl(lastk, L, 64);
+    return (int)((int64_t)g * SEG + (int64_t)L * LE + (kk < 0 ? 0 : kk));
+}
+
+// k_search: one workgroup per sequence.  Scans the segment sums for the one
+// segment holding u*S, then walks that segment lane by lane.
+template <int DTT, int DTD>
+__global__ __launch_bounds__(NT) void k_search(const Params P)
+{
+    const int b = blockIdx.x;
+    const SeqRec rec = P.rec[b];
+    if (rec.status != 1) return;
+    const int K = P.K, nseg = P.nseg;
+    const float s = P.s;
+    const int n = rec.n;
+    const bool bonus = n == K;
+    const char* trow = target_row<DTT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const float cp = shift_of(rec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
+    const float w = bonus ? 0.f : rec.zp / rec.zq;
+    __shared__ float sh_scan[NWAVE];
+    __shared__ int sh_seg[NWAVE];
+    __shared__ float sh_lo[1];
+
+    const float* sums_r = P.seg + (int64_t)b * nseg;
+    const float* sums_p = P.seg + ((int64_t)P.B + b) * nseg;
+    const Pick pk = find_segment<NT>(sums_r, sums_p, nseg, rec.u, bonus, sh_scan, sh_seg, sh_lo);
+    if ((threadIdx.x >> 6) == 0 && pk.g >= 0) {
+        const int y = walk_segment<DTT, DTD>(trow, drow, P.V, pk, s, cp, cq, w);
+        if (threadIdx.x == 0) {
+            P.out[(int64_t)b * (K + 1) + n] = y;
+            put(P.res_mass, b, pk.mode == 2 ? 0.f : pk.S / rec.zp);
         }
-        const uint64_t m = overrun ? 0ull : __ballot(cand >= 0);
-        int y;
-        if (m) {
-            const int L = __ffsll((unsigned long long)m) - 1;
-            y = (int)((int64_t)g * SEG + (int64_t)L * LE + __shfl(cand, L, 64));
+    }
+}
+
+// ------------------------------------ k_seq: one workgroup per sequence --
+//
+// One workgroup of QT threads owns sequence b and walks its positions itself:
+// it streams target row j and draft row j together, merges them on thread 0,
+// runs the test at j and stops at the first rejection, so rows past it are
+// never read and no other workgroup is ever waited for.  The decision, the
+// diagnostics and the draw from row n (its segment sums kept in LDS, the rows
+// just streamed likely still cached) follow in the same launch.  Fills the
+// chip when B is at least about the number of compute units.
+
+constexpr int QT = 1024;              // threads per workgroup: sixteen wave64
+constexpr int QW = QT / 64;
+constexpr int QU = 4;                 // 16-byte loads in flight per lane and row
+constexpr int QSPW = 4;               // draw: segments per wave per step
+constexpr int QMAXSEG = 4096;         // segment sums held in LDS: V <= QMAXSEG * SEG
+
+// Online softmax of elements [e0, e1) of target row trow and draft row drow
+// (may be null), both streamed in the same loop by BT threads with U 16-byte
+// loads in flight per lane and row.  e0 is a multiple of 8 elements; e1 is a
+// multiple of 8 or the row end.
+template <int DTT, int DTD, int BT, int U>
+__device__ __forceinline__ void stream_pair(const char* trow, const char* drow, int64_t e0, int64_t e1, float s,
+                                            SmState& st, SmState& sd)
+{
+    constexpr int ET = Fmt<DTT>::E, ED = Fmt<DTD>::E;
+    const int tid = threadIdx.x;
+    const bool al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0 &&
+                    (drow == nullptr || (reinterpret_cast<uintptr_t>(drow) & 15u) == 0);
+    if (al) {
+        const uint4* vt = reinterpret_cast<const uint4*>(trow);
+        const uint4* vd = reinterpret_cast<const uint4*>(drow);
+        const int64_t t0 = e0 / ET, t1 = e1 / ET;          // whole vectors of the range
+        const int64_t d0 = e0 / ED, d1 = drow ? e1 / ED : d0;
+        const int64_t nt = t1 - t0, nd = d1 - d0;
+        const int64_t nv = nt > nd ? nt : nd;
+        for (int64_t k = tid; k < nv; k += (int64_t)BT * U) {
+            uint4 rt[U], rd[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t vi = k + (int64_t)u * BT;
+                rt[u] = vi < nt ? vt[t0 + vi]
+                                : make_uint4(Fmt<DTT>::NEG_INF_WORD, Fmt<DTT>::NEG_INF_WORD,
+                                             Fmt<DTT>::NEG_INF_WORD, Fmt<DTT>::NEG_INF_WORD);
+            }
+            if (drow) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t vi = k + (int64_t)u * BT;
+                    rd[u] = vi < nd ? vd[d0 + vi]
+                                    : make_uint4(Fmt<DTD>::NEG_INF_WORD, Fmt<DTD>::NEG_INF_WORD,
+                                                 Fmt<DTD>::NEG_INF_WORD, Fmt<DTD>::NEG_INF_WORD);
+                }
+            }
+            if (k < nt) {
+                float x[U * ET];
+#pragma unroll
+                for (int u = 0; u < U; ++u) unpack<DTT>(rt[u], x + u * ET);
+                sm_window<U * ET>(x, s, st);
+            }
+            if (drow && k < nd) {
+                float x[U * ED];
+#pragma unroll
+                for (int u = 0; u < U; ++u) unpack<DTD>(rd[u], x + u * ED);
+                sm_window<U * ED>(x, s, sd);
+            }
+        }
+        const int64_t tt = t1 * ET;              // ragged tails (< E elements each)
+        if (tt + tid < e1) {
+            float x1[1] = {load1<DTT>(trow, tt + tid)};
+            sm_window<1>(x1, s, st);
+        }
+        if (drow) {
+            const int64_t dt = d1 * ED;
+            if (dt + tid < e1) {
+                float x1[1] = {load1<DTD>(drow, dt + tid)};
+                sm_window<1>(x1, s, sd);
+            }
+        }
+    } else {
+        constexpr int W = U * 4;
+        for (int64_t base = e0 + tid; base < e1; base += (int64_t)BT * W) {
+            float x[W], y[W];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int64_t i = base + (int64_t)k * BT;
+                x[k] = (i < e1) ? load1<DTT>(trow, i) : NEG_INF;
+                y[k] = (drow && i < e1) ? load1<DTD>(drow, i) : NEG_INF;
+            }
+            sm_window<W>(x, s, st);
+            if (drow) sm_window<W>(y, s, sd);
+        }
+    }
+}
+
+template <int DTT, int DTD>
+__global__ __launch_bounds__(QT) void k_seq(const Params P)
+{
+    const int b = blockIdx.x;
+    const int K = P.K, V = P.V, R = 2 * K + 1;
+    const float s = P.s;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    const bool has_draft = !greedy && P.draft != nullptr;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ RowStat f_rs[MAXR];
+    __shared__ TestIn ti[SV_MAX_K + 1];
+    __shared__ SmState sh_t[QW], sh_d[QW];
+    __shared__ AmState sh_a[QW];
+    __shared__ int sh_stop;
+    __shared__ Decision dec;
+    __shared__ float seg_r[QMAXSEG], seg_p[QMAXSEG];
+    __shared__ float sh_scan[QW];
+    __shared__ int sh_seg[QW];
+    __shared__ float sh_lo[1];
+
+    // rows never streamed stay invalid; the test inputs load while position 0
+    // streams (the first barrier below orders both before any read)
+    if (tid < R) f_rs[tid] = {0.f, 0.f, 0, 0};
+    const int tw = (QW - 1) * 64;                  // last wave loads the test inputs
+    if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
+
+    for (int j = 0; j <= K; ++j) {
+        const char* trow = target_row<DTT>(P, b, j);
+        const bool dj = has_draft && j < K;
+        if (greedy) {
+            SmState sm = {NEG_INF, 0.f};
+            AmState am = {NEG_INF, INT_MAX, 0u};
+            scan_chunk<DTT, true, QT, QU>(trow, 0, V, s, sm, am);
+            am = wave_reduce_am(am);
+            if (lane == 0) sh_a[wave] = am;
         } else {
-            int lastk = -1;
-#pragma unroll
-            for (int k = 0; k < LE; ++k)
-                if (wv[k] > 0.f) lastk = k;
-            const uint64_t mp = __ballot(lastk >= 0);
-            const int L = mp ? 63 - __clzll((long long)mp) : 0;
-            const int kk = __shfl(lastk, L, 64);
-            y = (int)((int64_t)g * SEG + (int64_t)L * LE + (kk < 0 ? 0 : kk));
+            SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
+            stream_pair<DTT, DTD, QT, QU>(trow, dj ? draft_row<DTD>(P, b, j) : nullptr, 0, V, s, st, sd);
+            st = wave_reduce_sm(st, s);
+            if (dj) sd = wave_reduce_sm(sd, s);
+            if (lane == 0) {
+                sh_t[wave] = st;
+                sh_d[wave] = sd;
+            }
         }
+        __syncthreads();
+        if (tid == 0) {
+            RowStat t, d = {0.f, 0.f, 0, 0};
+            if (greedy) {
+                AmState am = sh_a[0];
+                for (int w2 = 1; w2 < QW; ++w2) am = am_merge(am, sh_a[w2]);
+                t = rowstat_am(am);
+            } else {
+                SmState st = sh_t[0];
+                for (int w2 = 1; w2 < QW; ++w2) st = sm_merge(st, sh_t[w2], s);
+                t = rowstat_sm(st);
+                if (dj) {
+                    SmState sd = sh_d[0];
+                    for (int w2 = 1; w2 < QW; ++w2) sd = sm_merge(sd, sh_d[w2], s);
+                    d = rowstat_sm(sd);
+                    f_rs[K + 1 + j] = d;
+                }
+            }
+            f_rs[j] = t;
+            bool stop = true;
+            if (j < K) stop = test_from(V, s, greedy, t, d, ti[j].x, ti[j].u, ti[j].lx, ti[j].dx).stop;
+            sh_stop = stop;
+        }
+        __syncthreads();
+        if (sh_stop) break;
+    }
+
+    decide_core<DTT, DTD>(P, b, greedy, true, true, f_rs, ti, &dec);
+    if (greedy || !dec.ok) return;                 // uniform across the workgroup
+
+    // draw from row n: residual max(0, p - q) scaled by Z_p, or p for the bonus
+    const int n = dec.n, nseg = P.nseg;
+    const bool bonus = n == K;
+    const char* trow = target_row<DTT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const float cp = shift_of(dec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(dec.mq, s);
+    const float w = bonus ? 0.f : dec.zp / dec.zq;
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+    for (int g0 = wave * QSPW; g0 < nseg; g0 += QW * QSPW) {
+        float xl[QSPW][LE], xd[QSPW][LE];
+#pragma unroll
+        for (int k = 0; k < QSPW; ++k) {
+            const int64_t e = (int64_t)(g0 + k) * SEG + (int64_t)lane * LE;
+            load8<DTT>(trow, e, V, t_al, xl[k]);
+            if (!bonus) load8<DTD>(drow, e, V, d_al, xd[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < QSPW; ++k) {
+            float sr = 0.f, sp = 0.f;
+#pragma unroll
+            for (int q = 0; q < LE; ++q) {
+                const float ep = ex2(__builtin_fmaf(xl[k][q], s, -cp));
+                sp += ep;
+                sr += bonus ? ep : weight(xl[k][q], xd[k][q], s, cp, cq, w, 0);
+            }
+            sr = wave_sum(sr);
+            sp = wave_sum(sp);
+            if (lane == 0 && g0 + k < nseg) {
+                seg_r[g0 + k] = sr;
+                seg_p[g0 + k] = sp;
+            }
+        }
+    }
+    __syncthreads();
+    const Pick pk = find_segment<QT>(seg_r, seg_p, nseg, dec.u, bonus, sh_scan, sh_seg, sh_lo);
+    if (wave == 0) {
+        const int y = pk.g >= 0 ? walk_segment<DTT, DTD>(trow, drow, V, pk, s, cp, cq, w) : -1;
         if (lane == 0) {
             P.out[(int64_t)b * (K + 1) + n] = y;
-            put(P.res_mass, b, mode == 2 ? 0.f : S / rec.zp);
+            put(P.res_mass, b, pk.g < 0 ? NAN : (pk.mode == 2 ? 0.f : pk.S / dec.zp));
+        }
+    }
+}
+
+// ------------------------ k_seqg: G workgroups per sequence, one launch --
+//
+// The per-sequence walk of k_seq with each row split over the G workgroups of
+// the sequence (slice g: segments [g*gsegs, (g+1)*gsegs) of SEG elements), so
+// a sequence's later positions and its draw run on G compute units instead of
+// one.  After streaming its slice of position j a workgroup publishes its
+// partial statistics; every member waits for all G partials, merges them in
+// the same fixed order and takes the same decision bit for bit, so no member
+// ever needs another's decision.  The draw exchanges slice totals the same
+// way; the member whose slice holds u*S finds and walks the segment.
+//
+// Exchange: each published value travels in one 64-bit word with a 32-bit tag
+// in its upper half, stored and loaded as relaxed agent-scope atomics, so a
+// word is valid on its own and needs no fence.  Values go in pairs whose two
+// tags hash the sequence's call counter gep[b], the shape and the word's
+// index: a word left by an earlier call, or any other content, passes both
+// checks of a pair with probability 2^-64.  Member 0 advances gep[b] once all
+// G members have published position 0 (so all of them have read it).
+//
+// Waits spin on the loads with a bound; the host launches no more
+// workgroups than the device holds at once, so every member is resident and
+// the bound is never reached in practice.  A wait that reaches it marks the
+// sequence invalid (accepted_len -1) instead of hanging.
+
+constexpr int GT = 256;               // threads per workgroup
+constexpr int GW = GT / 64;
+constexpr int GU = 2;                 // 16-byte loads in flight per lane and row
+constexpr int GMAXG = 64;             // members per sequence at most (one wave gathers them)
+constexpr int GMAXSEG = 2048;         // segment sums of one slice held in LDS
+constexpr int GCAP = 4096;            // workgroups per launch at most (workspace sizing)
+constexpr int XCDS = 8;               // workgroup i runs on accelerator die i % 8
+constexpr int GSPIN = 1 << 20;        // polls before a wait gives up
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+__device__ __forceinline__ uint32_t word_tag(uint32_t ep, uint32_t salt, uint32_t widx)
+{
+    const uint32_t t = mix32(ep * 0x9e3779b9u ^ salt ^ mix32(widx + 0x632be5abu));
+    return t ? t : 1u;                // never 0: zeroed memory is never valid
+}
+
+__device__ __forceinline__ void put_word(uint64_t* w, uint32_t tag, uint32_t v)
+{
+    __hip_atomic_store(w, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t get_word(const uint64_t* w)
+{
+    return __hip_atomic_load(const_cast<uint64_t*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Word layout of one sequence's region: position j, member g, word w < 4 at
+// (j*G + g)*4 + w (target pair, then draft pair); draw totals of member g,
+// word w < 2 at (K+1)*G*4 + g*2 + w.
+__device__ __forceinline__ int pos_word(int K, int G, int j, int g, int w) { (void)K; return (j * G + g) * 4 + w; }
+__device__ __forceinline__ int draw_word(int K, int G, int g, int w) { return (K + 1) * G * 4 + g * 2 + w; }
+
+// Wave 0: lane l < G waits for the NW words of member l starting at word
+// index first(l) (consecutive), tags checked; v gets the values.  Returns
+// whether every member's words arrived (uniform over the wave).
+template <int NW>
+__device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t ep, uint32_t salt, int first,
+                                       uint32_t (&v)[NW])
+{
+    const int l = threadIdx.x & 63;
+    bool ready = l >= G;
+    uint32_t tg[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        tg[k] = word_tag(ep, salt, (uint32_t)(first + k));
+        v[k] = 0u;
+    }
+    for (int it = 0;; ++it) {
+        if (!ready) {
+            uint64_t w[NW];
+#pragma unroll
+            for (int k = 0; k < NW; ++k) w[k] = get_word(region + first + k);
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < NW; ++k) ok = ok && (uint32_t)(w[k] >> 32) == tg[k];
+            if (ok) {
+#pragma unroll
+                for (int k = 0; k < NW; ++k) v[k] = (uint32_t)w[k];
+                ready = true;
+            }
+        }
+        if (__all(ready)) return true;
+        if (it >= GSPIN) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+template <int DTT, int DTD>
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_seqg(const Params P)
+{
+    const int G = P.G;
+    const int xcd = (int)(blockIdx.x % XCDS), loc = (int)(blockIdx.x / XCDS);
+    const int q = loc / G;
+    const int b = xcd + XCDS * q;                  // members of a sequence share a die
+    const int g = loc - q * G;
+    if (b >= P.B) return;
+    const int K = P.K, V = P.V, R = 2 * K + 1;
+    const float s = P.s;
+    const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+    const bool has_draft = !greedy && P.draft != nullptr;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t salt = P.salt;
+    uint64_t* region = P.slots + (int64_t)b * (((int64_t)K + 1) * G * 4 + (int64_t)G * 2);
+    const int sg0 = g * P.gsegs;
+    const int sg1 = min(sg0 + P.gsegs, P.nseg);
+    const int nl = max(sg1 - sg0, 0);              // segments of this slice
+    const int64_t e0 = (int64_t)sg0 * SEG;
+    const int64_t e1 = min((int64_t)sg1 * SEG, (int64_t)V);
+
+    __shared__ RowStat f_rs[MAXR];
+    __shared__ TestIn ti[SV_MAX_K + 1];
+    __shared__ SmState sh_t[GW], sh_d[GW];
+    __shared__ AmState sh_a[GW];
+    __shared__ int sh_stop;                        // 0 go on, 1 stop, 2 a wait gave up
+    __shared__ Decision dec;
+    __shared__ float seg_r[GMAXSEG], seg_p[GMAXSEG];
+    __shared__ float sh_scan[GW];
+    __shared__ int sh_seg[GW];
+    __shared__ float sh_lo[1];
+    __shared__ int sh_pick_g, sh_pick_mode, sh_pick_over;
+    __shared__ float sh_pick_S, sh_pick_thr;
+
+    uint32_t ep = 0;
+    if (wave == 0) ep = (uint32_t)__hip_atomic_load(P.gep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < R) f_rs[tid] = {0.f, 0.f, 0, 0};
+    const int tw = (GW - 1) * 64;                  // last wave loads the test inputs
+    if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
+
+    int jb = 0;                                    // last position streamed
+    for (int j = 0; j <= K; ++j) {
+        jb = j;
+        const char* trow = target_row<DTT>(P, b, j);
+        const bool dj = has_draft && j < K;
+        if (greedy) {
+            SmState sm = {NEG_INF, 0.f};
+            AmState am = {NEG_INF, INT_MAX, 0u};
+            if (e0 < e1) scan_chunk<DTT, true, GT, GU>(trow, e0, e1, s, sm, am);
+            am = wave_reduce_am(am);
+            if (lane == 0) sh_a[wave] = am;
+        } else {
+            SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
+            if (e0 < e1) stream_pair<DTT, DTD, GT, GU>(trow, dj ? draft_row<DTD>(P, b, j) : nullptr, e0, e1, s, st, sd);
+            st = wave_reduce_sm(st, s);
+            if (dj) sd = wave_reduce_sm(sd, s);
+            if (lane == 0) {
+                sh_t[wave] = st;
+                sh_d[wave] = sd;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // this member's partial, merged over its waves in order, published
+            if (lane == 0) {
+                uint64_t* w = region + pos_word(K, G, j, g, 0);
+                const int wi = pos_word(K, G, j, g, 0);
+                if (greedy) {
+                    AmState am = sh_a[0];
+                    for (int w2 = 1; w2 < GW; ++w2) am = am_merge(am, sh_a[w2]);
+                    put_word(w, word_tag(ep, salt, wi), __float_as_uint(am.v));
+                    put_word(w + 1, word_tag(ep, salt, wi + 1), (uint32_t)am.i | (am.bad ? 0x80000000u : 0u));
+                } else {
+                    SmState st = sh_t[0], sd = sh_d[0];
+                    for (int w2 = 1; w2 < GW; ++w2) st = sm_merge(st, sh_t[w2], s);
+                    for (int w2 = 1; w2 < GW; ++w2) sd = sm_merge(sd, sh_d[w2], s);
+                    put_word(w, word_tag(ep, salt, wi), __float_as_uint(st.m));
+                    put_word(w + 1, word_tag(ep, salt, wi + 1), __float_as_uint(st.z));
+                    if (dj) {
+                        put_word(w + 2, word_tag(ep, salt, wi + 2), __float_as_uint(sd.m));
+                        put_word(w + 3, word_tag(ep, salt, wi + 3), __float_as_uint(sd.z));
+                    }
+                }
+            }
+            // all members' partials, merged in lane order on every member
+            bool ok;
+            RowStat t, d = {0.f, 0.f, 0, 0};
+            const int first = pos_word(K, G, j, lane, 0);
+            if (greedy) {
+                uint32_t v[2];
+                ok = gather<2>(region, G, ep, salt, first, v);
+                AmState am = {NEG_INF, INT_MAX, 0u};
+                if (lane < G) am = {__uint_as_float(v[0]), (int32_t)(v[1] & 0x7fffffffu), v[1] >> 31};
+                t = rowstat_am(wave_reduce_am(am));
+            } else if (dj) {
+                uint32_t v[4];
+                ok = gather<4>(region, G, ep, salt, first, v);
+                SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
+                if (lane < G) {
+                    st = {__uint_as_float(v[0]), __uint_as_float(v[1])};
+                    sd = {__uint_as_float(v[2]), __uint_as_float(v[3])};
+                }
+                t = rowstat_sm(wave_reduce_sm(st, s));
+                d = rowstat_sm(wave_reduce_sm(sd, s));
+            } else {
+                uint32_t v[2];
+                ok = gather<2>(region, G, ep, salt, first, v);
+                SmState st = {NEG_INF, 0.f};
+                if (lane < G) st = {__uint_as_float(v[0]), __uint_as_float(v[1])};
+                t = rowstat_sm(wave_reduce_sm(st, s));
+            }
+            // every member has read the counter once position 0 is in
+            if (j == 0 && g == 0 && lane == 0)
+                __hip_atomic_store(P.gep + b, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) {
+                f_rs[j] = t;
+                if (dj) f_rs[K + 1 + j] = d;
+                bool stop = true;
+                if (j < K) stop = test_from(V, s, greedy, t, d, ti[j].x, ti[j].u, ti[j].lx, ti[j].dx).stop;
+                sh_stop = ok ? (stop ? 1 : 0) : 2;
+            }
+        }
+        __syncthreads();
+        if (sh_stop) break;
+    }
+    (void)jb;
+    if (sh_stop == 2) {                            // a wait gave up
+        if (tid == 0) P.acc[b] = -1;
+        return;
+    }
+
+    decide_core<DTT, DTD>(P, b, greedy, g == 0, true, f_rs, ti, &dec);
+    if (greedy || !dec.ok) return;                 // uniform across the workgroup
+
+    // draw from row n: this member's slice of segment sums, then the totals
+    const int n = dec.n;
+    const bool bonus = n == K;
+    const char* trow = target_row<DTT>(P, b, n);
+    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const float cp = shift_of(dec.mp, s);
+    const float cq = bonus ? 0.f : shift_of(dec.mq, s);
+    const float w = bonus ? 0.f : dec.zp / dec.zq;
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+    for (int l0 = wave * SPW; l0 < nl; l0 += GW * SPW) {
+        float xl[SPW][LE], xd[SPW][LE];
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int64_t e = (int64_t)(sg0 + l0 + k) * SEG + (int64_t)lane * LE;
+            load8<DTT>(trow, e, V, t_al, xl[k]);
+            if (!bonus) load8<DTD>(drow, e, V, d_al, xd[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            float sr = 0.f, sp = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < LE; ++qq) {
+                const float ep2 = ex2(__builtin_fmaf(xl[k][qq], s, -cp));
+                sp += ep2;
+                sr += bonus ? ep2 : weight(xl[k][qq], xd[k][qq], s, cp, cq, w, 0);
+            }
+            sr = wave_sum(sr);
+            sp = wave_sum(sp);
+            if (lane == 0 && l0 + k < nl) {
+                seg_r[l0 + k] = sr;
+                seg_p[l0 + k] = sp;
+            }
+        }
+    }
+    __syncthreads();
+    float tr = 0.f, tp = 0.f;                      // slice totals, in the scan order the search uses
+    for (int base = 0; base < nl; base += GT) {
+        float tot;
+        block_incl_scan<GT>((base + tid < nl) ? seg_r[base + tid] : 0.f, sh_scan, &tot);
+        tr += tot;
+        block_incl_scan<GT>((base + tid < nl) ? seg_p[base + tid] : 0.f, sh_scan, &tot);
+        tp += tot;
+    }
+    if (wave == 0) {
+        if (lane == 0) {
+            const int wi = draw_word(K, G, g, 0);
+            put_word(region + wi, word_tag(ep, salt, wi), __float_as_uint(tr));
+            put_word(region + wi + 1, word_tag(ep, salt, wi + 1), __float_as_uint(tp));
+        }
+        uint32_t v[2];
+        const bool ok = gather<2>(region, G, ep, salt, draw_word(K, G, lane, 0), v);
+        const float mr = lane < G ? __uint_as_float(v[0]) : 0.f;
+        const float mp = lane < G ? __uint_as_float(v[1]) : 0.f;
+        // every lane walks the member totals in member order (same bits on all)
+        float S = 0.f;
+        for (int l = 0; l < G; ++l) S += __shfl(mr, l, 64);
+        int mode = bonus ? 1 : 0;
+        const bool use_p = !(S > 0.f);             // residual rounded to nothing: draw from p_n
+        if (use_p) {
+            mode = 2;
+            S = 0.f;
+            for (int l = 0; l < G; ++l) S += __shfl(mp, l, 64);
+        }
+        const float mine = use_p ? mp : mr;
+        const float thr = dec.u * S;
+        int gs = -1, over = 0;
+        float cum = 0.f, lo = 0.f;
+        for (int l = 0; l < G; ++l) {
+            const float v2 = __shfl(mine, l, 64);
+            if (gs < 0) {
+                if (v2 > 0.f && cum + v2 > thr) {
+                    gs = l;
+                    lo = cum;
+                } else {
+                    cum += v2;
+                }
+            }
+        }
+        if (gs < 0) {                              // rounding overrun: the last slice with weight
+            over = 1;
+            for (int l = G - 1; l >= 0; --l) {
+                const float v2 = __shfl(mine, l, 64);
+                if (gs < 0 && v2 > 0.f) gs = l;
+            }
+        }
+        if (lane == 0) {
+            sh_pick_g = ok ? gs : -2;
+            sh_pick_mode = mode;
+            sh_pick_over = over;
+            sh_pick_S = S;
+            sh_pick_thr = over ? POS_INF : thr - lo;
+        }
+    }
+    __syncthreads();
+    if (sh_pick_g == -2) {
+        if (tid == 0) P.acc[b] = -1;
+        return;
+    }
+    if (sh_pick_g != g) return;                    // another member's slice holds the draw
+    Pick pk;
+    pk.mode = sh_pick_mode;
+    pk.S = sh_pick_S;
+    const Locate L = locate_segment<GT>(pk.mode == 2 ? seg_p : seg_r, nl, sh_pick_thr, sh_scan, sh_seg, sh_lo);
+    pk.g = L.g < 0 ? -1 : sg0 + L.g;
+    pk.overrun = L.overrun || sh_pick_over;
+    pk.thr = sh_pick_thr;
+    pk.lo = L.lo;
+    if (wave == 0) {
+        const int y = pk.g >= 0 ? walk_segment<DTT, DTD>(trow, drow, V, pk, s, cp, cq, w) : -1;
+        if (lane == 0) {
+            P.out[(int64_t)b * (K + 1) + n] = y;
+            put(P.res_mass, b, pk.g < 0 ? NAN : (pk.mode == 2 ? 0.f : pk.S / dec.zp));
         }
     }
 }
 
 // -------------------------------------------------------------- host side --
 
+enum Sched { EAGER = 0, LAZY = 1, SEQ = 2 };
+
 struct Plan {
     int C, nseg, tiles;
+    Sched sched;
     bool lazy;
-    size_t off_rec, off_reach, off_part, off_seg, total;
+    int gmax;         // grouped per-sequence schedule: workgroups per sequence the workspace holds
+    int G, gsegs;     // and the ones this call uses (G < 2: one 1024-thread workgroup per sequence)
+    size_t off_rec, off_reach, off_part, off_seg, off_gep, off_slots, total;
 };
 
-// 0 = choose per call, 1 = eager, 2 = lazy (sv_set_mode; SV_MODE in the environment)
+// SV_MODE_AUTO / EAGER / LAZY / SEQ (sv_set_mode; SV_MODE in the environment)
 static std::atomic<int> g_mode{-1};
+// most workgroups per sequence under SV_MODE_SEQ, 0 = as many as fit
+// (sv_set_seq_groups; SV_SEQ_GROUPS in the environment)
+static std::atomic<int> g_groups{-1};
+
+static int groups_now()
+{
+    int m = g_groups.load(std::memory_order_relaxed);
+    if (m < 0) {
+        const char* e = getenv("SV_SEQ_GROUPS");
+        long v = e ? strtol(e, nullptr, 10) : 0;
+        m = (v >= 1 && v <= GMAXG) ? (int)v : 0;
+        int expect = -1;
+        g_groups.compare_exchange_strong(expect, m);
+        m = g_groups.load(std::memory_order_relaxed);
+    }
+    return m;
+}
 
 static int mode_now()
 {
     int m = g_mode.load(std::memory_order_relaxed);
     if (m < 0) {
         const char* e = getenv("SV_MODE");
-        m = (e && !strcmp(e, "eager")) ? 1 : (e && !strcmp(e, "lazy")) ? 2 : 0;
+        m = SV_MODE_AUTO;
+        if (e && !strcmp(e, "eager")) m = SV_MODE_EAGER;
+        if (e && !strcmp(e, "lazy")) m = SV_MODE_LAZY;
+        if (e && !strcmp(e, "seq")) m = SV_MODE_SEQ;
         int expect = -1;
         g_mode.compare_exchange_strong(expect, m);
         m = g_mode.load(std::memory_order_relaxed);
@@ -904,16 +1628,66 @@ static int mode_now()
     return m;
 }
 
-// Lazy mode pays one latency-bound launch per position (5-20 us each on
-// gfx950); it wins once the eager stream is long against K+1 such launches:
-// at least 64 MiB of logits per position.
-static bool choose_lazy(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd)
+static int64_t nseg_of(int32_t V) { return ((int64_t)V + SEG - 1) / SEG; }
+
+// Sequences are laid out eight to a die: the grouped launch has 8*ceil(B/8)
+// groups of G workgroups.
+static int64_t group_slots(int32_t B) { return 8 * (((int64_t)B + 7) / 8); }
+
+// Workgroups per sequence the workspace is sized for (device independent).
+static int group_max(int32_t B)
+{
+    const int64_t gm = GCAP / group_slots(B);
+    return (int)(gm < GMAXG ? gm : GMAXG);
+}
+
+// k_seqg workgroups the current device holds at once, per storage-type pair
+// (0 when unknown: the grouped launch is then not used).
+template <int DTT, int DTD>
+static int group_capacity_t()
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static std::atomic<int> cache[64];
+    static std::atomic<bool> init[64];
+    if (init[dev].load(std::memory_order_acquire)) return cache[dev].load(std::memory_order_relaxed);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD>), GT,
+                                                     0) != hipSuccess)
+        return 0;
+    cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+    init[dev].store(true, std::memory_order_release);
+    return cus * per_cu;
+}
+
+static int group_capacity(int32_t dtt, int32_t dtd)
+{
+    if (dtt == SV_BF16 && dtd == SV_BF16) return group_capacity_t<SV_BF16, SV_BF16>();
+    if (dtt == SV_F32 && dtd == SV_F32) return group_capacity_t<SV_F32, SV_F32>();
+    if (dtt == SV_F32 && dtd == SV_BF16) return group_capacity_t<SV_F32, SV_BF16>();
+    return group_capacity_t<SV_BF16, SV_F32>();
+}
+
+// Automatic choice.  The per-sequence schedule (one launch, no row past a
+// rejection read, draws overlapping other sequences' streams) wins once
+// position 0 alone streams at least 64 MiB, enough to fill the chip; it
+// needs the vocabulary's segment sums to fit in LDS.  Otherwise lazy mode,
+// which pays one latency-bound launch per position (5-20 us each on
+// gfx950), wins once the eager stream is long against K+1 such launches: at
+// least 64 MiB of logits per position; else eager.
+static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd)
 {
     const int m = mode_now();
-    if (m == 1 || K == 0) return false;
-    if (m == 2) return true;
-    const double bytes = (double)B * V * ((double)(K + 1) * (dtt == SV_BF16 ? 2 : 4) + (double)K * (dtd == SV_BF16 ? 2 : 4));
-    return bytes >= (double)(K + 1) * 64.0 * (1 << 20);
+    const bool seq_ok = nseg_of(V) <= QMAXSEG;
+    if (m == SV_MODE_SEQ) return seq_ok ? SEQ : (K == 0 ? EAGER : LAZY);
+    if (m == SV_MODE_EAGER) return EAGER;
+    if (m == SV_MODE_LAZY) return K == 0 ? EAGER : LAZY;
+    const double bt = dtt == SV_BF16 ? 2 : 4, bd = dtd == SV_BF16 ? 2 : 4;
+    const double mib64 = 64.0 * (1 << 20);
+    if (seq_ok && (double)B * V * (bt + (K > 0 ? bd : 0.0)) >= mib64) return SEQ;
+    if (K == 0) return EAGER;
+    const double bytes = (double)B * V * ((double)(K + 1) * bt + (double)K * bd);
+    return bytes >= (double)(K + 1) * mib64 ? LAZY : EAGER;
 }
 
 static int env_int(const char* name, int dflt)
@@ -927,8 +1701,9 @@ static int env_int(const char* name, int dflt)
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static bool make_plan(int32_t B, int32_t K, int32_t V, bool lazy, Plan* pl)
+static bool make_plan(int32_t B, int32_t K, int32_t V, Sched sched, Plan* pl)
 {
+    const bool lazy = sched == LAZY;
     const int64_t R = 2 * (int64_t)K + 1;
     const int64_t rows = (int64_t)B * R;
     const int64_t rows_per_launch = lazy ? (int64_t)B * 2 : rows;
@@ -942,6 +1717,7 @@ static bool make_plan(int32_t B, int32_t K, int32_t V, bool lazy, Plan* pl)
     if (C > max_c) C = max_c;
     if (C < 1) C = 1;
     pl->C = (int)C;
+    pl->sched = sched;
     pl->lazy = lazy;
     pl->nseg = (int)(((int64_t)V + SEG - 1) / SEG);
     pl->tiles = (pl->nseg + SPT - 1) / SPT;
@@ -951,6 +1727,12 @@ static bool make_plan(int32_t B, int32_t K, int32_t V, bool lazy, Plan* pl)
     pl->off_reach = o; o = align_up(o + sizeof(int32_t) * (size_t)B, 256);
     pl->off_part = o; o = align_up(o + sizeof(Partial) * (size_t)(rows * C), 256);
     pl->off_seg = o;  o = align_up(o + sizeof(float) * 2 * (size_t)B * (size_t)pl->nseg, 256);
+    pl->gmax = group_max(B);
+    pl->G = 1;
+    pl->gsegs = pl->nseg;
+    pl->off_gep = o;  o = align_up(o + sizeof(uint32_t) * (size_t)B, 256);
+    pl->off_slots = o;
+    o = align_up(o + sizeof(uint64_t) * (size_t)B * (size_t)pl->gmax * (((size_t)K + 1) * 4 + 2), 256);
     pl->total = o;
     return true;
 }
@@ -984,7 +1766,7 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
         for (const float* q : d)
             if (q && !aligned_to(q, 4)) return SV_EINVAL;
     }
-    if (!make_plan(B, K, V, choose_lazy(B, K, V, dtt, dtd), pl)) return SV_EINVAL;
+    if (!make_plan(B, K, V, choose_sched(B, K, V, dtt, dtd), pl)) return SV_EINVAL;
     if (!ws || !aligned_to(ws, 16) || ws_bytes < pl->total) return SV_EWORKSPACE;
     char* w = static_cast<char*>(ws);
     P->target = target;
@@ -1010,12 +1792,45 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->nseg = pl->nseg;
     P->tiles = pl->tiles;
     P->s = s;
+    P->gep = reinterpret_cast<uint32_t*>(w + pl->off_gep);
+    P->slots = reinterpret_cast<uint64_t*>(w + pl->off_slots);
+    P->G = 1;
+    P->gsegs = pl->nseg;
+    P->salt = 0;
+    if (pl->sched == SEQ) {
+        // as many workgroups per sequence as fit on the device at once (each
+        // waits for the others), within the workspace's and LDS's limits
+        int64_t G = group_capacity(dtt, dtd) / group_slots(B);
+        if (G > pl->gmax) G = pl->gmax;
+        const int lim = groups_now();
+        if (lim > 0 && G > lim) G = lim;
+        if (G > pl->nseg) G = pl->nseg;
+        int64_t gsegs = G >= 2 ? (pl->nseg + G - 1) / G : pl->nseg;
+        if (G >= 2 && gsegs <= GMAXSEG) {
+            pl->G = (int)G;
+            pl->gsegs = (int)gsegs;
+            uint32_t h = 0x811c9dc5u;
+            const uint32_t f[7] = {(uint32_t)B, (uint32_t)K, (uint32_t)V, (uint32_t)G, (uint32_t)dtt,
+                                   (uint32_t)dtd, (uint32_t)gsegs};
+            for (uint32_t x : f) h = (h ^ x) * 0x01000193u;
+            P->G = pl->G;
+            P->gsegs = pl->gsegs;
+            P->salt = h;
+        }
+    }
     return 1;   // ready to launch
 }
 
 template <int DTT, int DTD>
 static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
 {
+    if (pl.sched == SEQ) {                         // the whole step in one launch
+        if (pl.G >= 2)
+            hipLaunchKernelGGL((k_seqg<DTT, DTD>), dim3((unsigned)(group_slots(P.B) * pl.G)), dim3(GT), 0, st, P);
+        else
+            hipLaunchKernelGGL((k_seq<DTT, DTD>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
+        return;
+    }
     if (!pl.lazy) {
         const dim3 grid((unsigned)((int64_t)P.B * (2 * P.K + 1) * pl.C));
         hipLaunchKernelGGL((k_rowstats<DTT, DTD>), grid, dim3(NT), 0, st, P);
@@ -1030,6 +1845,7 @@ static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
 template <int DTT, int DTD>
 static void launch_draw_t(const Params& P, const Plan& pl, hipStream_t st)
 {
+    if (pl.sched == SEQ) return;                   // k_seq already drew
     hipLaunchKernelGGL((k_decide<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
     hipLaunchKernelGGL((k_tiles<DTT, DTD>), dim3((unsigned)((int64_t)P.B * pl.tiles)), dim3(NT), 0, st, P);
     hipLaunchKernelGGL((k_search<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
@@ -1086,7 +1902,7 @@ size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
 {
     if (B <= 0 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(dtype)) return 0;
     sv::Plan pe, pz;
-    if (!sv::make_plan(B, K, V, false, &pe) || !sv::make_plan(B, K, V, true, &pz)) return 0;
+    if (!sv::make_plan(B, K, V, sv::EAGER, &pe) || !sv::make_plan(B, K, V, sv::LAZY, &pz)) return 0;
     return pe.total > pz.total ? pe.total : pz.total;
 }
 
@@ -1160,12 +1976,46 @@ int sv_sample(const void* logits, int32_t dtype, const float* uniforms, float te
 
 int sv_set_mode(int mode)
 {
-    if (mode < 0 || mode > 2) return SV_EINVAL;
+    if (mode < SV_MODE_AUTO || mode > SV_MODE_SEQ) return SV_EINVAL;
     sv::g_mode.store(mode, std::memory_order_relaxed);
     return SV_OK;
 }
 
 int sv_get_mode(void) { return sv::mode_now(); }
+
+int sv_set_seq_groups(int groups)
+{
+    if (groups < 0 || groups > sv::GMAXG) return SV_EINVAL;
+    sv::g_groups.store(groups, std::memory_order_relaxed);
+    return SV_OK;
+}
+
+int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype)
+{
+    if (B < 1 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(target_dtype) || !sv::dtype_ok(draft_dtype))
+        return SV_EINVAL;
+    if (sv::choose_sched(B, K, V, target_dtype, draft_dtype) != sv::SEQ) return 0;
+    // the plan of a call on dummy (aligned, non-null) pointers, nothing launched
+    sv::Params P;
+    sv::Plan pl;
+    alignas(16) static char dummy[16];
+    const int rc = sv::prepare(dummy, dummy, reinterpret_cast<const int32_t*>(dummy),
+                               reinterpret_cast<const float*>(dummy), 1.f, nullptr, B, K, V, target_dtype,
+                               draft_dtype, reinterpret_cast<int32_t*>(dummy), reinterpret_cast<int32_t*>(dummy),
+                               nullptr, dummy, (size_t)-1, &P, &pl);
+    return rc == 1 ? pl.G : SV_EINVAL;
+}
+
+int sv_schedule(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype)
+{
+    if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(target_dtype) || !sv::dtype_ok(draft_dtype))
+        return SV_EINVAL;
+    switch (sv::choose_sched(B, K, V, target_dtype, draft_dtype)) {
+    case sv::SEQ: return SV_MODE_SEQ;
+    case sv::LAZY: return SV_MODE_LAZY;
+    default: return SV_MODE_EAGER;
+    }
+}
 
 const char* sv_strerror(int code)
 {

@@ -301,11 +301,3 @@ def reached_bytes(w: Workload, accepted_len: np.ndarray) -> int:
         if not w.greedy[b]:
             tot += min(m + 1, K) * V * s
     return tot
-
-
-def lazy_schedule(w: Workload) -> bool:
-    """Whether the library's automatic schedule streams positions lazily for
-    this shape (one eager pass would read at least 64 MiB per position)."""
-    if w.K == 0:
-        return False
-    return w.B * w.V * (2 * w.K + 1) * w.elem_bytes >= (w.K + 1) * 64 * (1 << 20)

@@ -142,9 +142,9 @@ def test_fused_verify_checks_everything_before_launch(lib, kw):
 
 
 def test_mode_knob(lib):
-    assert lib.sv_set_mode(3) == binding.SV_EINVAL and lib.sv_set_mode(-1) == binding.SV_EINVAL
+    assert lib.sv_set_mode(4) == binding.SV_EINVAL and lib.sv_set_mode(-1) == binding.SV_EINVAL
     old = lib.sv_get_mode()
-    for m in (binding.MODE_EAGER, binding.MODE_LAZY, binding.MODE_AUTO):
+    for m in (binding.MODE_EAGER, binding.MODE_LAZY, binding.MODE_SEQ, binding.MODE_AUTO):
         assert lib.sv_set_mode(m) == binding.SV_OK and lib.sv_get_mode() == m
     lib.sv_set_mode(old)
 
@@ -153,7 +153,56 @@ def test_workspace_covers_both_schedules(lib):
     # one workspace must serve either schedule for the same shape
     a = binding.workspace_bytes(256, 8, 152064, binding.SV_BF16)
     old = lib.sv_get_mode()
-    for m in (binding.MODE_EAGER, binding.MODE_LAZY):
+    for m in (binding.MODE_EAGER, binding.MODE_LAZY, binding.MODE_SEQ):
         lib.sv_set_mode(m)
         assert binding.workspace_bytes(256, 8, 152064, binding.SV_BF16) == a
     lib.sv_set_mode(old)
+
+
+def test_schedule_query(lib):
+    old = lib.sv_get_mode()
+    try:
+        bf = binding.SV_BF16
+        lib.sv_set_mode(binding.MODE_SEQ)
+        assert binding.schedule(256, 8, 152064, bf) == binding.MODE_SEQ
+        assert binding.schedule(4, 0, 2048 * 512, bf) == binding.MODE_SEQ          # largest LDS-resident vocabulary
+        assert binding.schedule(4, 2, 2048 * 1024 + 1, bf) == binding.MODE_LAZY    # beyond it
+        lib.sv_set_mode(binding.MODE_EAGER)
+        assert binding.schedule(256, 8, 152064, bf) == binding.MODE_EAGER
+        lib.sv_set_mode(binding.MODE_LAZY)
+        assert binding.schedule(256, 8, 152064, bf, binding.SV_F32) == binding.MODE_LAZY
+        assert binding.schedule(256, 0, 152064, bf) == binding.MODE_EAGER          # nothing to skip at K = 0
+        lib.sv_set_mode(binding.MODE_AUTO)
+        assert binding.schedule(2, 3, 1000, bf) == binding.MODE_EAGER
+        assert binding.schedule(256, 8, 152064, bf) == binding.MODE_SEQ           # 148 MiB at position 0
+        assert binding.schedule(256, 0, 152064, bf) == binding.MODE_SEQ           # sampling step, 74 MiB
+        assert binding.schedule(64, 5, 128256, bf) == binding.MODE_EAGER          # 31 MiB
+        assert binding.schedule(64, 8, 2048 * 1024 + 1, bf) == binding.MODE_LAZY  # past the LDS limit
+        for bad in ((1, 64, 10, bf), (1, 1, 0, bf), (-1, 1, 10, bf), (1, 1, 10, 7)):
+            with pytest.raises(binding.SpecVerifyError):
+                binding.schedule(*bad)
+    finally:
+        lib.sv_set_mode(old)
+
+
+def test_seq_group_knob(lib):
+    old = lib.sv_get_mode()
+    try:
+        bf = binding.SV_BF16
+        for bad in (-1, 65):
+            with pytest.raises(binding.SpecVerifyError):
+                binding.set_seq_groups(bad)
+        lib.sv_set_mode(binding.MODE_LAZY)
+        assert binding.seq_groups(256, 8, 152064, bf) == 0            # not the per-sequence schedule
+        lib.sv_set_mode(binding.MODE_SEQ)
+        for cap in (0, 1, 3):
+            binding.set_seq_groups(cap)
+            g = binding.seq_groups(256, 8, 152064, bf)
+            assert g >= 1 and (cap == 0 or g <= cap)
+        binding.set_seq_groups(0)
+        assert binding.seq_groups(3, 2, 300, bf) == 1                 # one segment: nothing to split
+        with pytest.raises(binding.SpecVerifyError):
+            binding.seq_groups(0, 2, 300, bf)
+    finally:
+        lib.sv_set_mode(old)
+        binding.set_seq_groups(0)

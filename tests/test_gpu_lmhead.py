@@ -80,7 +80,19 @@ def test_gemm_rejects_bad_shapes(dev):
         binding.lmhead(h, wt)          # d = 12 is not a multiple of 8
 
 
-def test_fused_lmhead_verify_full_size(dev):
+@pytest.mark.parametrize("mode,groups", [(binding.MODE_AUTO, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1)],
+                         ids=["auto", "seq", "seq1"])
+def test_fused_lmhead_verify_full_size(dev, mode, groups):
+    binding.set_mode(mode)
+    binding.set_seq_groups(groups)
+    try:
+        _fused_case(dev)
+    finally:
+        binding.set_mode(binding.MODE_AUTO)
+        binding.set_seq_groups(0)
+
+
+def _fused_case(dev):
     import torch
     w = I.cfg_lmhead()
     _log(f"[lmhead] {w.name}: generated")

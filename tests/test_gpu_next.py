@@ -31,9 +31,21 @@ def _log(msg):
 
 # ----------------------------------------------------------- sampling step --
 
+@pytest.mark.parametrize("mode,groups", [(binding.MODE_AUTO, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1)],
+                         ids=["auto", "seq", "seq1"])
 @pytest.mark.parametrize("B,V,dtype,T", [(64, 50000, I.BF16, 0.7), (7, 1001, I.F32, 1.3), (300, 152064, I.BF16, 1.0),
                                          (5, 1, I.F32, 1.0)])
-def test_sample_matches_oracle(dev, B, V, dtype, T):
+def test_sample_matches_oracle(dev, B, V, dtype, T, mode, groups):
+    binding.set_mode(mode)
+    binding.set_seq_groups(groups)
+    try:
+        _sample_case(dev, B, V, dtype, T)
+    finally:
+        binding.set_mode(binding.MODE_AUTO)
+        binding.set_seq_groups(0)
+
+
+def _sample_case(dev, B, V, dtype, T):
     import torch
     mask = (np.arange(B) % 3 == 0).astype(np.uint8)
     w = I.synth_logits(900 + B, B, 0, V, dtype=dtype, T=T, sigma=3.0, zipf=True, draft_scale=1.0,

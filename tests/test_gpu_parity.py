@@ -227,19 +227,26 @@ def test_gpu_output_law_chi_square(dev):
 
 
 # ---------------------------------------------------------------------------
-# Both row-statistics schedules (eager: every row; lazy: one launch per
-# position, rows past the first rejection never read) against the oracle.
+# Every schedule (eager: every row; lazy: one launch per position, rows past
+# the first rejection never read; seq: one workgroup per sequence walking its
+# own positions) against the oracle.
 # ---------------------------------------------------------------------------
 
 @pytest.fixture
 def schedule(dev, request):
-    binding.set_mode(request.param)
+    mode, groups = request.param
+    binding.set_mode(mode)
+    binding.set_seq_groups(groups)
     yield request.param
     binding.set_mode(binding.MODE_AUTO)
+    binding.set_seq_groups(0)
 
 
-SCHED = pytest.mark.parametrize("schedule", [binding.MODE_EAGER, binding.MODE_LAZY],
-                                indirect=True, ids=["eager", "lazy"])
+# seq: as many workgroups per sequence as the device holds; seq1: one
+# 1024-thread workgroup per sequence
+SCHED = pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.MODE_LAZY, 0), (binding.MODE_SEQ, 0),
+                                             (binding.MODE_SEQ, 1)],
+                                indirect=True, ids=["eager", "lazy", "seq", "seq1"])
 
 
 @SCHED
@@ -271,9 +278,29 @@ def test_schedules_deterministic_and_split(dev, schedule):
     test_deterministic_and_split_launches(dev)
 
 
+@SCHED
+def test_schedules_output_law(dev, schedule):
+    test_gpu_output_law_chi_square(dev)
+
+
+@SCHED
+@pytest.mark.parametrize("target_f32", [False, True], ids=["bf16_f32", "f32_bf16"])
+@pytest.mark.parametrize("V", [30000, 30001])
+def test_schedules_mixed_storage(dev, schedule, target_f32, V):
+    """Target and draft logits in different storage types (spec_verify_ex)."""
+    mask = (np.arange(12) % 4 == 1).astype(np.uint8)
+    w = I.synth_logits(41 + V, 12, 4, V, dtype=I.BF16, T=0.8, sigma=3.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=0.4, greedy_mask=mask, name=f"mixed_{V}")
+    tgt, drf, dt = w.target, I.bf16_bits_to_f32(w.draft), I.BF16
+    if target_f32:
+        tgt, drf, dt = I.bf16_bits_to_f32(w.target), w.draft, I.F32
+    check(I.Workload(w.name, w.B, w.K, w.V, dt, w.T, tgt, drf, w.tokens, w.uniforms, w.greedy), dev)
+
+
 def test_lazy_reads_only_reached_rows(dev):
-    """A NaN planted in a row after the first rejection is never read in lazy
-    mode (the eager stream reads it but the method ignores it; both agree)."""
+    """A NaN planted in a row after the first rejection is never read by the
+    lazy and per-sequence schedules (the eager stream reads it but the method
+    ignores it; all agree)."""
     import torch
     w = I.cfg_152k(B=16)
     o = oracle.verify(w)
@@ -283,10 +310,23 @@ def test_lazy_reads_only_reached_rows(dev):
         if n + 1 <= w.K:
             t[b, n + 1:, :] = 0x7FC0
     w2 = I.Workload(w.name, w.B, w.K, w.V, w.dtype, w.T, t, w.draft, w.tokens, w.uniforms, w.greedy)
-    for m in (binding.MODE_EAGER, binding.MODE_LAZY):
+    for m, groups in ((binding.MODE_EAGER, 0), (binding.MODE_LAZY, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1)):
         binding.set_mode(m)
+        binding.set_seq_groups(groups)
         try:
             g = run_gpu(w2, dev)
         finally:
             binding.set_mode(binding.MODE_AUTO)
+            binding.set_seq_groups(0)
         parity.compare(w2, g, o)
+
+
+def test_seq_beyond_lds_vocab_uses_lazy(dev):
+    """Vocabularies past the per-sequence schedule's LDS limit run lazily."""
+    w = I.synth_logits(8, 2, 2, 2_100_001, dtype=I.BF16, T=1.0, sigma=2.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=0.3, name="seq_big_vocab")
+    binding.set_mode(binding.MODE_SEQ)
+    try:
+        check(w, dev)
+    finally:
+        binding.set_mode(binding.MODE_AUTO)
