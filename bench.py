@@ -254,6 +254,53 @@ def bench_sample(args, torch, np, binding, I, dev):
     return w, g, res, "sample"
 
 
+def bench_lookup(args, torch, np, binding, I, dev):
+    """Prompt lookup: the proposer over B=256 histories of 2-4k tokens, then the
+    verify step on its candidates (one-hot proposals) over [256, 9, 152064] bf16."""
+    lw = I.lookup_152k()
+    print(f"[bench] workload {lw.name}: generated", file=sys.stderr, flush=True)
+    hist = torch.from_numpy(lw.history).to(dev)
+    hl = torch.from_numpy(lw.hist_len).to(dev)
+    tt = torch.from_numpy(lw.target.view(np.int16)).view(torch.bfloat16).to(dev)
+    uni = torch.from_numpy(lw.uniforms).to(dev)
+    call = binding.BoundLookup(hist, hl, lw.n_max, lw.n_min, tt, uni, lw.T)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        call.propose()
+        call.verify()
+    ms, prop_ms, ver_ms = _timed(torch, stream, args.steps, call.propose, call.verify)
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    klen = call.klen.cpu().numpy()
+    out = call.outputs
+    acc = out["accepted_len"].cpu().numpy()
+    gpu = {k: v.cpu().numpy() for k, v in out.items()}
+    gpu["_cand"], gpu["_klen"] = call.cand.cpu().numpy(), klen
+    s = 2
+    # the verify launches stream target rows 0..klen[b] once and row n once more for the draw
+    rows = int(np.sum(np.maximum(klen, 0) + 1))
+    ver_bytes = (rows + int(np.sum(acc >= 0))) * lw.V * s
+    hist_bytes = int(lw.hist_len.sum()) * 4
+    w = I.Workload(lw.name, lw.B, lw.K, lw.V, lw.dtype, lw.T, lw.target, np.zeros((lw.B, lw.K, 0), np.uint16),
+                   gpu["_cand"], lw.uniforms, lw.greedy, seed=lw.seed)
+    w.lookup = lw
+    res = _base_result(w, args.steps, args.warmup, ms, "f32")
+    res["config"] = {"workload": lw.name, "B": lw.B, "K": lw.K, "V": lw.V, "logits": "bf16",
+                     "history_tokens": int(lw.hist_len.sum()), "n_max": lw.n_max, "n_min": lw.n_min,
+                     "temperature": lw.T, "seed": lw.seed, "schedule": "eager (one-hot proposals)"}
+    v_s = float(ver_ms.mean()) * 1e-3
+    res["roofline"] = {"bound": "hbm", "achieved": ver_bytes / v_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": ver_bytes / v_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                       "kernel": "spec_verify_lookup (k_rowstats + k_decide + k_tiles + k_search)",
+                       "algorithmic_bytes_per_launch": ver_bytes, "avg_launch_ms": float(ver_ms.mean()),
+                       "proposer_avg_ms": float(prop_ms.mean()), "proposer_history_bytes": hist_bytes,
+                       "proposer_gbs": hist_bytes / (float(prop_ms.mean()) * 1e-3) / 1e9}
+    res["timing_ms"] = {"propose_median": float(np.median(prop_ms)), "verify_median": float(np.median(ver_ms)),
+                        "step_events_median": float(np.median(prop_ms + ver_ms))}
+    res["method"] = _method_stats(w, acc)
+    res["method"]["candidates_hist"] = np.bincount(np.maximum(klen, 0), minlength=lw.K + 1).tolist()
+    return w, gpu, res, "lookup"
+
+
 def bench_kvcommit(args, torch, np, binding, I, dev):
     """KV-cache commit: 64 planes (32 layers x keys/values) of 2048-byte rows
     (8 heads x 128 x bf16), B=256, K=8, staging block = previous final token +
@@ -301,7 +348,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="cfg152k",
-                    choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead", "sample", "kvcommit"])
+                    choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead", "sample", "kvcommit", "lookup"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing (repeated whole-workload calls)")
@@ -335,10 +382,42 @@ def main() -> int:
                       "seq": binding.MODE_SEQ}[args.mode])
     binding.set_seq_groups(args.seq_groups)
 
-    fn = {"lmhead": bench_lmhead, "sample": bench_sample, "kvcommit": bench_kvcommit}.get(args.config, bench_verify)
+    fn = {"lmhead": bench_lmhead, "sample": bench_sample, "kvcommit": bench_kvcommit,
+          "lookup": bench_lookup}.get(args.config, bench_verify)
     w, gpu, result, kind = fn(args, torch, np, binding, I, dev)
 
     if kind == "kv":
+        result["cpu_baseline"] = None
+    elif kind == "lookup" and not args.no_cpu_baseline:
+        import oracle
+        from oracle import lookup, parity
+        oracle.build(force=False)
+        lw = w.lookup
+        pick = np.arange(16)                       # bounded sample: the first 16 sequences
+        t_start = time.perf_counter()
+        ts = []
+        while len(ts) < 2 or time.perf_counter() - t_start < args.cpu_seconds:
+            t0 = time.perf_counter()
+            co, ko = lookup.propose(lw.history[pick], lw.hist_len[pick], lw.n_max, lw.n_min, lw.K)
+            orc = lookup.verify_lookup(I.logits_as_f64(lw.target[pick], lw.dtype), co, ko, lw.uniforms[pick],
+                                       lw.T, lw.greedy[pick], len(pick), lw.K, lw.V)
+            ts.append(time.perf_counter() - t0)
+        med = float(np.median(ts))
+        result["cpu_baseline"] = {"value": len(pick) * (lw.K + 1) * lw.V / med, "unit": "logits/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"first 16 of {lw.B} sequences (proposer + one-hot verify), "
+                                            f"{len(ts)} calls, median {med * 1e3:.1f} ms, python proposer + fp64 C "
+                                            f"verify, 1 thread; scaled to verified logits/s"}
+        ok = np.array_equal(gpu["_klen"][pick], ko) and np.array_equal(gpu["_cand"][pick], co)
+        try:
+            sub = {k: v[pick] for k, v in gpu.items() if not k.startswith("_")}
+            wsub = I.Workload(w.name, len(pick), w.K, w.V, w.dtype, w.T, None, None, co, None, lw.greedy[pick])
+            rep = parity.compare(wsub, sub, orc)
+            result["parity"] = {"ok": ok, "flagged": rep["flagged"], "sample": "first 16 sequences",
+                                "flagged_mismatch": len(rep["flagged_mismatch"]), "invalid": rep["invalid"]}
+        except parity.ParityError as e:
+            result["parity"] = {"ok": False, "error": str(e)[:500]}
+    elif kind == "lookup":
         result["cpu_baseline"] = None
     elif not args.no_cpu_baseline:
         import oracle

@@ -77,6 +77,7 @@ extern "C" {
 #define SV_ELAUNCH    -3
 
 #define SV_MAX_K 63
+#define SV_MAX_NGRAM 64
 
 /* Optional diagnostics: a host struct of device pointers, each may be NULL.
  * Entries the method never examines (positions after the first rejection,
@@ -212,6 +213,40 @@ int sv_sample(const void* logits, int32_t dtype, const float* uniforms, float te
 int sv_kv_commit(void* cache, int32_t* cache_len, const void* staged, const int32_t* accepted_len,
                  int32_t planes, int32_t B, int32_t K, int32_t offset, int64_t l_max, int64_t row_bytes,
                  int32_t* status, void* stream);
+
+/* ---- prompt lookup ------------------------------------------------------
+ * Candidates without a draft model ([QH] "Vấn đề 3: Làm sao khi không muốn
+ * train drafter?": the continuation of an earlier occurrence of the text's
+ * ending, then target verification).
+ *
+ * sv_lookup_propose: history [B, Lmax] int32 token ids, row b holding
+ *   hist_len[b] tokens (prompt and output so far).  For n = n_max down to
+ *   n_min, the first n whose last-n-token ending occurs earlier in the
+ *   history with at least one token after the occurrence wins; the earliest
+ *   such occurrence is used.  Outputs cand [B, K] int32 (the up to K tokens
+ *   after it, clipped at the history's end, then -1) and klen [B] int32 (how
+ *   many; 0 without a match; -1 when hist_len[b] is outside [0, Lmax]).
+ *   EINVAL on B < 0, Lmax < 0, n_min < 1, n_max < n_min, n_max >
+ *   SV_MAX_NGRAM, K outside [0, SV_MAX_K], NULL or misaligned (4 B) arrays.
+ * spec_verify_lookup: the verify step on such candidates.  A deterministic
+ *   proposal is a one-hot draft distribution (all of q on the proposed
+ *   token), so with [MC] "Приёмка и почему распределение НЕ портится" a
+ *   sampling sequence accepts x_j iff u[b,j] < p_j(x_j), and after a
+ *   rejection draws from p_n without x_n (renormalised); greedy sequences
+ *   compare with the argmax.  Sequence b has klen[b] candidates (cand
+ *   [B, K], entries past klen[b] never read): after klen[b] acceptances the
+ *   bonus token comes from p_{klen[b]}; column K of the uniforms drives the
+ *   final draw in every case; target rows past klen[b] are never read.
+ *   klen[b] outside [0, K] marks the sequence invalid (accepted_len -1).
+ *   Other arguments, outputs, workspace and errors as spec_verify (no draft
+ *   logits; q_tok reports 1 and lse_q 0 for tested positions); always the
+ *   eager schedule.                                                       */
+int sv_lookup_propose(const int32_t* history, const int32_t* hist_len, int32_t B, int32_t Lmax,
+                      int32_t n_max, int32_t n_min, int32_t K, int32_t* cand, int32_t* klen, void* stream);
+int spec_verify_lookup(const void* target_logits, int32_t dtype, const int32_t* cand, const int32_t* klen,
+                       const float* uniforms, float temperature, const uint8_t* greedy_flag,
+                       int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                       const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Row-statistics schedule, process-wide (thread-safe; a tuning knob: every
  * schedule meets the same definition, though float sums taken in another

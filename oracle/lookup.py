@@ -11,7 +11,9 @@ then the target verifies them.  The page leaves the details open; readings:
 * an earlier occurrence starts at i with i + n <= L - 1 (at least one token
   follows it inside the history); the earliest such i is taken;
 * the candidates are the up to K tokens after it, clipped at the end of the
-  history; no occurrence gives no candidates.
+  history; no occurrence gives no candidates; a history length outside
+  [0, Lmax] is invalid input (klen -1, which the verify step reports as an
+  invalid sequence).
 
 Verification ([MC] "Приёмка и почему распределение НЕ портится", [QH]
 "Giải pháp"): a deterministic proposal is the draft distribution q that puts
@@ -40,6 +42,9 @@ def propose(history: np.ndarray, hist_len: np.ndarray, n_max: int, n_min: int, K
     klen = np.zeros(B, np.int32)
     for b in range(B):
         L = int(hist_len[b])
+        if L < 0 or L > history.shape[1]:
+            klen[b] = -1
+            continue
         h = [int(t) for t in history[b, :L]]
         for n in range(min(n_max, L - 1), n_min - 1, -1):
             suffix = h[L - n:]

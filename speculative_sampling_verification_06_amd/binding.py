@@ -24,6 +24,7 @@ SV_MAX_K = 63
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups",
+           "sv_lookup_propose", "spec_verify_lookup",
            "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
 
@@ -76,6 +77,13 @@ def load_library(path: str = LIB_PATH):
             lib.sv_kv_commit.restype = C.c_int
             lib.sv_kv_commit.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+            lib.sv_lookup_propose.restype = C.c_int
+            lib.sv_lookup_propose.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 5 + [C.c_void_p] * 3
+            lib.spec_verify_lookup.restype = C.c_int
+            lib.spec_verify_lookup.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                               C.c_float, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                               C.c_void_p, C.c_void_p, C.POINTER(SvDiag), C.c_void_p,
+                                               C.c_size_t, C.c_void_p]
             lib.sv_set_mode.restype = C.c_int
             lib.sv_set_mode.argtypes = [C.c_int]
             lib.sv_get_mode.restype = C.c_int
@@ -487,6 +495,117 @@ def sample(logits, uniforms, temperature, greedy=None, *, lse=False, stream=None
                             tokens.data_ptr() if B else None, None if out_lse is None else out_lse.data_ptr(),
                             ws.data_ptr(), ws.numel(), stream))
     return (tokens, out_lse) if lse else tokens
+
+
+# ------------------------------------------------------------ prompt lookup --
+
+def lookup_propose(history, hist_len, n_max, n_min, K, *, cand=None, klen=None, stream=None):
+    """Candidates from the history [B, Lmax] int32 (hist_len [B] int32 tokens per row):
+    returns (cand [B, K] int32 padded with -1, klen [B] int32)."""
+    torch = _torch()
+    B, Lmax = history.shape
+    dev = history.device
+    _dev_ptr(history, "history", torch.int32, (B, Lmax))
+    _dev_ptr(hist_len, "hist_len", torch.int32, (B,))
+    if cand is None:
+        cand = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if klen is None:
+        klen = torch.empty(B, dtype=torch.int32, device=dev)
+    _dev_ptr(cand, "cand", torch.int32, (B, K))
+    _dev_ptr(klen, "klen", torch.int32, (B,))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check_rc(load_library().sv_lookup_propose(
+        history.data_ptr() if history.numel() else None, hist_len.data_ptr() if B else None, B, Lmax,
+        int(n_max), int(n_min), int(K), cand.data_ptr() if cand.numel() else None,
+        klen.data_ptr() if B else None, stream))
+    return cand, klen
+
+
+def verify_lookup(target, cand, klen, uniforms, temperature, greedy=None, *, diag=True, workspace=None,
+                  stream=None):
+    """spec_verify_lookup: the verify step on prompt-lookup candidates (one-hot proposals)."""
+    torch = _torch()
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target logits must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _dtype_code(target)
+    dev = target.device
+    _dev_ptr(target, "target_logits", shape=(B, K + 1, V))
+    _dev_ptr(cand, "cand", torch.int32, (B, K))
+    _dev_ptr(klen, "klen", torch.int32, (B,))
+    _dev_ptr(uniforms, "uniforms", torch.float32, (B, K + 1))
+    if greedy is not None:
+        _dev_ptr(greedy, "greedy_flag", torch.uint8, (B,))
+    outputs = Outputs(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                      out_tokens=torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+    dg = None
+    if diag:
+        outputs.update(p_tok=torch.empty(B, K, dtype=torch.float32, device=dev),
+                       q_tok=torch.empty(B, K, dtype=torch.float32, device=dev),
+                       lse_p=torch.empty(B, K + 1, dtype=torch.float32, device=dev),
+                       lse_q=torch.empty(B, K, dtype=torch.float32, device=dev),
+                       res_mass=torch.empty(B, dtype=torch.float32, device=dev))
+        dg = SvDiag(*[_dev_ptr(outputs[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
+    need = lib.sv_workspace_bytes(B, K, V, dt)
+    ws = workspace if workspace is not None else get_workspace(need, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check_rc(lib.spec_verify_lookup(
+        target.data_ptr() if B else None, dt, _dev_ptr(cand, "cand"), _dev_ptr(klen, "klen"),
+        _dev_ptr(uniforms, "uniforms"), C.c_float(float(temperature)), _dev_ptr(greedy, "greedy_flag"), B, K, V,
+        _dev_ptr(outputs["accepted_len"], "accepted_len"), _dev_ptr(outputs["out_tokens"], "out_tokens"),
+        None if dg is None else C.byref(dg), ws.data_ptr(), ws.numel(), stream))
+    return outputs
+
+
+class BoundLookup:
+    """Prompt lookup bound to fixed device tensors: propose() fills cand/klen
+    from the history, verify() runs spec_verify_lookup on them; each is one
+    pre-marshalled ctypes call."""
+
+    def __init__(self, history, hist_len, n_max, n_min, target, uniforms, temperature, greedy=None, *,
+                 diag=True, stream=None):
+        torch = _torch()
+        lib = load_library()
+        B, K1, V = target.shape
+        K = K1 - 1
+        self.cand, self.klen = lookup_propose(history, hist_len, n_max, n_min, K, stream=stream)
+        self.outputs = verify_lookup(target, self.cand, self.klen, uniforms, temperature, greedy, diag=diag,
+                                     stream=stream)
+        torch.cuda.synchronize(target.device)
+        dt = _dtype_code(target)
+        o = self.outputs
+        self._dg = None
+        if "p_tok" in o:
+            self._dg = SvDiag(*[_dev_ptr(o[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
+        ws = get_workspace(lib.sv_workspace_bytes(B, K, V, dt), target.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(target.device).cuda_stream
+        self._keep = (history, hist_len, target, uniforms, greedy, ws)
+        Lmax = history.shape[1]
+        self._pargs = (C.c_void_p(_dev_ptr(history, "history")), C.c_void_p(_dev_ptr(hist_len, "hist_len")),
+                       C.c_int32(B), C.c_int32(Lmax), C.c_int32(n_max), C.c_int32(n_min), C.c_int32(K),
+                       C.c_void_p(_dev_ptr(self.cand, "cand")), C.c_void_p(_dev_ptr(self.klen, "klen")),
+                       C.c_void_p(stream))
+        self._vargs = (C.c_void_p(target.data_ptr()), C.c_int32(dt), C.c_void_p(_dev_ptr(self.cand, "cand")),
+                       C.c_void_p(_dev_ptr(self.klen, "klen")), C.c_void_p(uniforms.data_ptr()),
+                       C.c_float(float(temperature)), C.c_void_p(_dev_ptr(greedy, "greedy_flag")),
+                       C.c_int32(B), C.c_int32(K), C.c_int32(V),
+                       C.c_void_p(o["accepted_len"].data_ptr()), C.c_void_p(o["out_tokens"].data_ptr()),
+                       None if self._dg is None else C.byref(self._dg),
+                       C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel()), C.c_void_p(stream))
+        self._propose, self._verify = lib.sv_lookup_propose, lib.spec_verify_lookup
+
+    def propose(self):
+        _check_rc(self._propose(*self._pargs))
+        return self.cand, self.klen
+
+    def verify(self):
+        _check_rc(self._verify(*self._vargs))
+        return self.outputs
 
 
 # --------------------------------------------------------------- KV commit --

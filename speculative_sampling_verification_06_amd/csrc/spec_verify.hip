@@ -79,12 +79,14 @@ struct Partial {      // one (row, chunk): softmax {m, z} or argmax {m = value, 
     uint32_t bad;
 };
 
-struct SeqRec {       // what k_decide (tile 0) leaves for k_search
+struct SeqRec {       // what k_decide leaves for k_tiles and k_search
     int32_t n;
     int32_t status;   // 1 = sampling sequence, valid, draw pending
     float mp, zp;     // target row n
-    float mq, zq;     // draft row n (n < K)
+    float mq, zq;     // draft row n (n below the sequence's proposal count)
     float u;          // uniforms[b, K]
+    int32_t bonus;    // n equals the proposal count: draw from p_n
+    int32_t xn;       // one-hot proposals: the token proposed at n (its draft row is implicit)
     int32_t pad;
 };
 
@@ -111,6 +113,8 @@ struct Params {
     int32_t nseg, tiles;
     int32_t G, gsegs; // grouped schedule: workgroups per sequence, segments per workgroup slice
     uint32_t salt;    // grouped schedule: shape hash folded into the tags
+    const int32_t* klen;  // proposals per sequence (prompt lookup), null = K for all
+    int32_t onehot;   // draft distribution = one-hot at the proposed token (no draft logits)
     float s;          // log2(e) / T
 };
 
@@ -451,6 +455,10 @@ __global__ __launch_bounds__(NT) void k_rowstats(const Params P)
     __shared__ AmState sh_am[NWAVE];
 
     if (is_draft && (greedy || P.draft == nullptr)) return;      // never read
+    if (!is_draft && P.klen) {                                   // rows past the proposals: never examined
+        const int kb = P.klen[b];
+        if (kb < 0 || kb > K || r > kb) return;
+    }
     const int64_t cl = chunk_len(P.V, P.C);
     const int64_t e0 = (int64_t)c * cl;
     const int64_t e1 = e0 + cl < (int64_t)P.V ? e0 + cl : (int64_t)P.V;
@@ -550,10 +558,10 @@ template <int DTT, int DTD>
 __device__ __forceinline__ TestOut position_test(const Params& P, int b, int j, bool greedy, const RowStat& t,
                                                  const RowStat& d, int32_t x, float u)
 {
-    float lx = 0.f, dx = 0.f;
+    float lx = 0.f, dx = 0.f;                      // one-hot proposals: the draft logit at x is 0
     if (!greedy && t.ok && d.ok && x >= 0 && x < P.V && u >= 0.f && u < 1.f) {
         lx = load1<DTT>(target_row<DTT>(P, b, j), x);
-        dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
+        if (!P.onehot) dx = load1<DTD>(draft_row<DTD>(P, b, j), x);
     }
     return test_from(P.V, P.s, greedy, t, d, x, u, lx, dx);
 }
@@ -570,7 +578,7 @@ __device__ __forceinline__ TestIn load_test_in(const Params& P, int b, int j, bo
         r.x = P.tokens[(int64_t)b * K + j];
         if (!greedy && r.x >= 0 && r.x < P.V) {
             r.lx = load1<DTT>(target_row<DTT>(P, b, j), r.x);
-            if (P.draft) r.dx = load1<DTD>(draft_row<DTD>(P, b, j), r.x);
+            if (P.draft && !P.onehot) r.dx = load1<DTD>(draft_row<DTD>(P, b, j), r.x);
         }
     }
     return r;
@@ -597,10 +605,15 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
     if (tid < 64) {
         const int j = tid;
         const int64_t ub = (int64_t)b * (K + 1);
+        // proposals of this sequence: K, or its own count (prompt lookup)
+        const int Kb = P.klen ? P.klen[b] : K;
+        const bool kb_bad = Kb < 0 || Kb > K;
         bool stop = false, inval = false;
         float ptok = NAN, qtok = NAN;
         int32_t x = -1;
-        if (j < K) {
+        if (j < K && (kb_bad || j >= Kb)) {
+            stop = true;                           // past the proposals: no test
+        } else if (j < K) {
             TestOut o;
             if (ti) {
                 x = ti[j].x;
@@ -618,9 +631,10 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
         const uint64_t smask = __ballot(stop);
         const uint64_t imask = __ballot(inval);
         const int n = smask ? (__ffsll((unsigned long long)smask) - 1) : K;
-        bool bad = (n < K) && ((imask >> n) & 1ull);
+        bool bad = kb_bad || ((n < K) && ((imask >> n) & 1ull));
+        const bool at_end = n == Kb;               // every proposal accepted: the bonus row
         float uK = 0.f;
-        if (!bad && n == K) bad = !f_rs[K].ok;
+        if (!bad && at_end) bad = !f_rs[n].ok;
         if (!bad && !greedy) {
             uK = ti ? ti[K].u : P.uniforms[ub + K];
             bad = !(uK >= 0.f && uK < 1.f);
@@ -630,8 +644,8 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
             dec->ok = !bad;
             dec->mp = bad || greedy ? 0.f : f_rs[n].m;
             dec->zp = bad || greedy ? 1.f : f_rs[n].z;
-            dec->mq = (bad || greedy || n == K) ? 0.f : f_rs[K + 1 + n].m;
-            dec->zq = (bad || greedy || n == K) ? 1.f : f_rs[K + 1 + n].z;
+            dec->mq = (bad || greedy || at_end) ? 0.f : f_rs[K + 1 + n].m;
+            dec->zq = (bad || greedy || at_end) ? 1.f : f_rs[K + 1 + n].z;
             dec->u = uK;
         }
         if (write_out) {
@@ -652,11 +666,12 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
                 const bool drawn_later = draw_here && !greedy && j == n;
                 if (j <= K && !drawn_later) out[j] = (j < n) ? x : ((j == n && greedy) ? f_rs[n].i : -1);
                 const bool seen = !greedy && j <= n;
+                const bool seen_q = seen && j < Kb;      // draft row j examined (tested)
                 if (j < K) {
                     put(P.p_tok, (int64_t)b * K + j, seen ? ptok : NAN);
                     put(P.q_tok, (int64_t)b * K + j, seen ? qtok : NAN);
                     put(P.lse_q, (int64_t)b * K + j,
-                        seen ? (shift_of(f_rs[K + 1 + j].m, s) + log2f(f_rs[K + 1 + j].z)) * LN2 : NAN);
+                        seen_q ? (shift_of(f_rs[K + 1 + j].m, s) + log2f(f_rs[K + 1 + j].z)) * LN2 : NAN);
                 }
                 if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_rs[j].m, s) + log2f(f_rs[j].z)) * LN2 : NAN);
                 if (j == 0) {
@@ -664,15 +679,17 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
                     if (greedy) put(P.res_mass, b, 0.f);
                 }
             }
-            if (j == 0 && !draw_here) {
+            if (j == n && !draw_here) {           // lane n holds x_n
                 SeqRec r;
                 r.n = n;
                 r.status = (!bad && !greedy) ? 1 : 0;
                 r.mp = f_rs[n].m;
                 r.zp = greedy ? 1.f : f_rs[n].z;
-                r.mq = (greedy || n == K) ? 0.f : f_rs[K + 1 + n].m;
-                r.zq = (greedy || n == K) ? 1.f : f_rs[K + 1 + n].z;
+                r.mq = (greedy || at_end) ? 0.f : f_rs[K + 1 + n].m;
+                r.zq = (greedy || at_end) ? 1.f : f_rs[K + 1 + n].z;
                 r.u = uK;
+                r.bonus = at_end ? 1 : 0;
+                r.xn = x;
                 r.pad = 0;
                 P.rec[b] = r;
             }
@@ -692,7 +709,8 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
     if (tid < R) {
         const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
         const bool draft_row_ = tid > K;
-        if (draft_row_ && (greedy || P.draft == nullptr)) f_rs[tid] = {0.f, 0.f, 0, 0};
+        if (draft_row_ && P.onehot) f_rs[tid] = {0.f, 1.f, 0, 1};   // logit 0 at x_j, -inf elsewhere
+        else if (draft_row_ && (greedy || P.draft == nullptr)) f_rs[tid] = {0.f, 0.f, 0, 0};
         else f_rs[tid] = merge_row(pp, C, P.s, greedy);
     }
     __syncthreads();
@@ -768,6 +786,16 @@ __device__ __forceinline__ float weight(float l, float d, float s, float cp, flo
     return fmaxf(0.f, __builtin_fmaf(-w, eq, ep));
 }
 
+// Draw inputs of a one-hot draft row (all of q on the proposed token x): -inf
+// (q = 0) away from x; at x the residual max(0, p(x) - 1) is exactly 0, which
+// +inf gives in weight() (fma(-w, +inf, e_p) = -inf, then max with 0), free
+// of the rounding of Z_p.
+__device__ __forceinline__ void onehot8(int64_t e, int32_t x, float* xd)
+{
+#pragma unroll
+    for (int k = 0; k < LE; ++k) xd[k] = (e + k == (int64_t)x) ? POS_INF : NEG_INF;
+}
+
 // k_decide: one workgroup per sequence settles n and writes the outputs and
 // the record the draw launches read.
 template <int DTT, int DTD>
@@ -790,12 +818,13 @@ __global__ __launch_bounds__(NT) void k_tiles(const Params P)
     const SeqRec rec = P.rec[b];
     if (rec.status != 1) return;                    // greedy, invalid: nothing to draw
 
-    const int K = P.K, V = P.V, nseg = P.nseg;
+    const int V = P.V, nseg = P.nseg;
     const float s = P.s;
     const int n = rec.n;
-    const bool bonus = n == K;
+    const bool bonus = rec.bonus != 0;
+    const bool oh = P.onehot != 0;
     const char* trow = target_row<DTT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const char* drow = (bonus || oh) ? nullptr : draft_row<DTD>(P, b, n);
     const float cp = shift_of(rec.mp, s);
     const float cq = bonus ? 0.f : shift_of(rec.mq, s);
     const float w = bonus ? 0.f : rec.zp / rec.zq;
@@ -809,7 +838,10 @@ __global__ __launch_bounds__(NT) void k_tiles(const Params P)
         const int seg = t * SPT + wave * SPW + k;
         const int64_t e = (int64_t)seg * SEG + (int64_t)lane * LE;
         load8<DTT>(trow, e, V, t_al, xl[k]);
-        if (!bonus) load8<DTD>(drow, e, V, d_al, xd[k]);
+        if (!bonus) {
+            if (oh) onehot8(e, rec.xn, xd[k]);
+            else load8<DTD>(drow, e, V, d_al, xd[k]);
+        }
     }
 #pragma unroll
     for (int k = 0; k < SPW; ++k) {
@@ -937,9 +969,11 @@ __device__ Pick find_segment(const float* sums_r, const float* sums_p, int nseg,
 // One segment on one wave: lane exclusive prefix, then an in-lane walk.  Only
 // a positive weight can be chosen; a segment with a positive sum always holds
 // one.  Returns the drawn index on every lane.
+
+// ox >= 0: the draft row is one-hot at token ox (drow unused).
 template <int DTT, int DTD>
 __device__ int walk_segment(const char* trow, const char* drow, int V, const Pick& pk, float s, float cp,
-                            float cq, float w)
+                            float cq, float w, int32_t ox = -1)
 {
     const int lane = threadIdx.x & 63;
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
@@ -948,7 +982,10 @@ __device__ int walk_segment(const char* trow, const char* drow, int V, const Pic
     const int64_t e = (int64_t)g * SEG + (int64_t)lane * LE;
     float xl[LE], xd[LE], wv[LE];
     load8<DTT>(trow, e, V, t_al, xl);
-    if (mode == 0) load8<DTD>(drow, e, V, d_al, xd);
+    if (mode == 0) {
+        if (ox >= 0) onehot8(e, ox, xd);
+        else load8<DTD>(drow, e, V, d_al, xd);
+    }
     float ls = 0.f;
 #pragma unroll
     for (int k = 0; k < LE; ++k) {
@@ -990,9 +1027,10 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
     const int K = P.K, nseg = P.nseg;
     const float s = P.s;
     const int n = rec.n;
-    const bool bonus = n == K;
+    const bool bonus = rec.bonus != 0;
+    const bool oh = P.onehot != 0;
     const char* trow = target_row<DTT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const char* drow = (bonus || oh) ? nullptr : draft_row<DTD>(P, b, n);
     const float cp = shift_of(rec.mp, s);
     const float cq = bonus ? 0.f : shift_of(rec.mq, s);
     const float w = bonus ? 0.f : rec.zp / rec.zq;
@@ -1004,7 +1042,7 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
     const float* sums_p = P.seg + ((int64_t)P.B + b) * nseg;
     const Pick pk = find_segment<NT>(sums_r, sums_p, nseg, rec.u, bonus, sh_scan, sh_seg, sh_lo);
     if ((threadIdx.x >> 6) == 0 && pk.g >= 0) {
-        const int y = walk_segment<DTT, DTD>(trow, drow, P.V, pk, s, cp, cq, w);
+        const int y = walk_segment<DTT, DTD>(trow, drow, P.V, pk, s, cp, cq, w, (oh && !bonus) ? rec.xn : -1);
         if (threadIdx.x == 0) {
             P.out[(int64_t)b * (K + 1) + n] = y;
             put(P.res_mass, b, pk.mode == 2 ? 0.f : pk.S / rec.zp);
@@ -1742,10 +1780,11 @@ static bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintp
 static bool dtype_ok(int32_t dt) { return dt == SV_F32 || dt == SV_BF16; }
 static size_t dtype_bytes(int32_t dt) { return dt == SV_BF16 ? 2 : 4; }
 
+// force: a schedule the call must use (-1: the mode's choice).
 static int prepare(const void* target, const void* draft, const int32_t* tokens, const float* uniforms,
                    float T, const uint8_t* greedy, int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd,
                    int32_t* acc, int32_t* out, const sv_diag* diag, void* ws, size_t ws_bytes,
-                   Params* P, Plan* pl)
+                   Params* P, Plan* pl, int force = -1)
 {
     (void)greedy;
     if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
@@ -1766,7 +1805,8 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
         for (const float* q : d)
             if (q && !aligned_to(q, 4)) return SV_EINVAL;
     }
-    if (!make_plan(B, K, V, choose_sched(B, K, V, dtt, dtd), pl)) return SV_EINVAL;
+    const Sched sched = force >= 0 ? (Sched)force : choose_sched(B, K, V, dtt, dtd);
+    if (!make_plan(B, K, V, sched, pl)) return SV_EINVAL;
     if (!ws || !aligned_to(ws, 16) || ws_bytes < pl->total) return SV_EWORKSPACE;
     char* w = static_cast<char*>(ws);
     P->target = target;
@@ -1797,6 +1837,8 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->G = 1;
     P->gsegs = pl->nseg;
     P->salt = 0;
+    P->klen = nullptr;
+    P->onehot = 0;
     if (pl->sched == SEQ) {
         // as many workgroups per sequence as fit on the device at once (each
         // waits for the others), within the workspace's and LDS's limits
@@ -1972,6 +2014,27 @@ int sv_sample(const void* logits, int32_t dtype, const float* uniforms, float te
     sv_diag dg = {nullptr, nullptr, lse, nullptr, nullptr};
     return sv_verify_mixed(logits, nullptr, nullptr, uniforms, temperature, greedy_flag, B, 0, V, dtype, dtype,
                            acc, tokens, lse ? &dg : nullptr, workspace, w0, stream, 0);
+}
+
+int spec_verify_lookup(const void* target_logits, int32_t dtype, const int32_t* cand, const int32_t* klen,
+                       const float* uniforms, float temperature, const uint8_t* greedy_flag, int32_t B, int32_t K,
+                       int32_t V, int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag, void* workspace,
+                       size_t workspace_bytes, void* stream)
+{
+    // the eager launches with one-hot draft rows that are never stored and
+    // target rows past each sequence's proposals skipped
+    sv::Params P;
+    sv::Plan pl;
+    if (B > 0 && (!klen || (reinterpret_cast<uintptr_t>(klen) & 3u))) return SV_EINVAL;
+    int rc = sv::prepare(target_logits, nullptr, cand, uniforms, temperature, greedy_flag, B, K, V, dtype, dtype,
+                         accepted_len, out_tokens, diag, workspace, workspace_bytes, &P, &pl, sv::EAGER);
+    if (rc <= 0) return rc;
+    P.klen = klen;
+    P.onehot = 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = sv::launch_stats(P, pl, dtype, dtype, st);
+    if (rc != SV_OK) return rc;
+    return sv::launch_draw(P, pl, dtype, dtype, st);
 }
 
 int sv_set_mode(int mode)

@@ -301,3 +301,84 @@ def reached_bytes(w: Workload, accepted_len: np.ndarray) -> int:
         if not w.greedy[b]:
             tot += min(m + 1, K) * V * s
     return tot
+
+
+# ---------------------------------------------------------------------------
+# Prompt-lookup workloads (no draft model).
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LookupWorkload:
+    """Token histories for the proposer plus the target logits that verify
+    its candidates (host side)."""
+    name: str
+    B: int
+    K: int
+    V: int
+    dtype: int
+    T: float
+    history: np.ndarray      # [B, Lmax] int32 (row b valid up to hist_len[b])
+    hist_len: np.ndarray     # [B] int32
+    n_max: int
+    n_min: int
+    target: np.ndarray       # [B, K+1, V] stored logits
+    uniforms: np.ndarray     # [B, K+1] fp32
+    greedy: np.ndarray       # [B] uint8
+    seed: int = 0
+
+
+def synth_lookup(seed: int, B: int, K: int, V: int, Lmax: int, *, dtype: int, T: float = 1.0,
+                 prompt_frac: float = 0.75, edit_rate: float = 0.02, agree: float = 0.8, bump: float = 12.0,
+                 sigma: float = 3.0, n_max: int = 4, n_min: int = 1, greedy_mask: np.ndarray | None = None,
+                 name: str = "lookup") -> LookupWorkload:
+    """The code-editing pattern of a prompt-lookup workload: a prompt of
+    Zipf(1.1)-distributed token ids, then an output that re-types a span of it,
+    each copied token replaced by a random id with probability edit_rate.
+    History lengths are drawn in [Lmax/2, Lmax].  Target logits follow the
+    generic recipe (N(0, sigma) + the log-Zipf bias); at each of the first K
+    positions, with probability `agree`, the token the copied span continues
+    with gets `bump` added (a target that mostly agrees with the copy).  The
+    generator knows that token from the span it copied, not from any proposer.
+    """
+    history = np.zeros((B, Lmax), np.int32)
+    hist_len = np.zeros(B, np.int32)
+    target = np.empty((B, K + 1, V), dtype={F32: np.float32, BF16: np.uint16}[dtype])
+    uniforms = np.empty((B, K + 1), np.float32)
+    greedy = np.zeros(B, np.uint8) if greedy_mask is None else greedy_mask.astype(np.uint8)
+    bias = zipf_bias(V)
+    pz = np.exp(bias.astype(np.float64))
+    pz /= pz.sum()
+    cz = np.cumsum(pz)
+    seeds = _seq_seeds(seed, B, 4)
+
+    def one(b):
+        r_h, r_l, r_a, r_u = (np.random.Generator(np.random.PCG64(s)) for s in seeds[b])
+        L = int(r_h.integers(max(2, Lmax // 2), Lmax + 1)) if Lmax >= 2 else Lmax
+        P = max(1, int(L * prompt_frac))
+        prompt = np.minimum(np.searchsorted(cz, r_h.random(P + K + 1)), V - 1).astype(np.int32)
+        out_len = L - P
+        start = int(r_h.integers(0, max(1, P - out_len)))
+        src = prompt[start:start + out_len + K + 1]
+        out = src[:out_len].copy()
+        edits = r_h.random(out_len) < edit_rate
+        out[edits] = r_h.integers(0, V, size=int(edits.sum()))
+        h = np.concatenate([prompt[:P], out])[:L]
+        history[b, :L] = h
+        hist_len[b] = L
+        l = r_l.standard_normal((K + 1, V), dtype=np.float32) * np.float32(sigma) + bias
+        nxt = src[out_len:out_len + K]                  # what the copied span continues with
+        for j in range(min(K, len(nxt))):
+            if r_a.random() < agree:
+                l[j, nxt[j]] += np.float32(bump)
+        target[b] = _store(l, dtype)
+        uniforms[b] = grid_uniforms(r_u, (K + 1,))
+
+    with ThreadPoolExecutor(max_workers=min(_WORKERS, max(1, B))) as ex:
+        list(ex.map(one, range(B)))
+    return LookupWorkload(name=name, B=B, K=K, V=V, dtype=dtype, T=T, history=history, hist_len=hist_len,
+                          n_max=n_max, n_min=n_min, target=target, uniforms=uniforms, greedy=greedy, seed=seed)
+
+
+def lookup_152k(seed: int = 1005, B: int = 256) -> LookupWorkload:
+    """B=256 histories of 2048-4096 tokens, K=8, V=152064 bf16, T=1, sampling."""
+    return synth_lookup(seed, B, 8, 152064, 4096, dtype=BF16, name=f"lookup_B{B}_K8_V152064_L4096_bf16")

@@ -70,6 +70,12 @@ def test_propose_matches_substring_search(alphabet):
         assert _prop(seq, n_max, n_min, K) == _by_string_search(seq, n_max, n_min, K), (seq, n_max, n_min, K)
 
 
+def test_propose_invalid_length():
+    h = np.array([[1, 2, 1, 2], [1, 2, 1, 2], [1, 2, 1, 2]], np.int32)
+    cand, klen = lookup.propose(h, np.array([-1, 5, 4]), 2, 1, 3)
+    assert klen.tolist() == [-1, -1, 2] and np.all(cand[:2] == -1)
+
+
 def test_propose_batched_rows_are_independent():
     rng = np.random.default_rng(5)
     B, Lmax = 9, 50
