@@ -594,7 +594,9 @@ __device__ __forceinline__ TestIn load_test_in(const Params& P, int b, int j, bo
 // draw_here leaves out_tokens[b, n] and res_mass of a sampling sequence to a
 // draw in the same workgroup.  Every thread must call it; *dec is valid for
 // all threads on return.
-template <int DTT, int DTD>
+// RAGGED: per-sequence proposal counts P.klen (prompt lookup); compiled out
+// of the plain verify step.
+template <int DTT, int DTD, bool RAGGED = false>
 __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out, bool draw_here,
                             const RowStat* f_rs, const TestIn* ti, Decision* dec)
 {
@@ -606,8 +608,8 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
         const int j = tid;
         const int64_t ub = (int64_t)b * (K + 1);
         // proposals of this sequence: K, or its own count (prompt lookup)
-        const int Kb = P.klen ? P.klen[b] : K;
-        const bool kb_bad = Kb < 0 || Kb > K;
+        const int Kb = RAGGED ? P.klen[b] : K;
+        const bool kb_bad = RAGGED && (Kb < 0 || Kb > K);
         bool stop = false, inval = false;
         float ptok = NAN, qtok = NAN;
         int32_t x = -1;
@@ -714,7 +716,8 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         else f_rs[tid] = merge_row(pp, C, P.s, greedy);
     }
     __syncthreads();
-    decide_core<DTT, DTD>(P, b, greedy, write_out, false, f_rs, nullptr, dec);
+    if (P.klen) decide_core<DTT, DTD, true>(P, b, greedy, write_out, false, f_rs, nullptr, dec);
+    else decide_core<DTT, DTD, false>(P, b, greedy, write_out, false, f_rs, nullptr, dec);
 }
 
 // --------------------------- k_rowstats_lazy: position j, live rows only --
@@ -1144,7 +1147,9 @@ __device__ __forceinline__ void stream_pair(const char* trow, const char* drow, 
     }
 }
 
-template <int DTT, int DTD>
+// OH: one-hot proposals (prompt lookup), a separate instance so the plain
+// verify step's register budget is unaffected.
+template <int DTT, int DTD, bool OH = false>
 __global__ __launch_bounds__(QT) void k_seq(const Params P)
 {
     const int b = blockIdx.x;
@@ -1152,6 +1157,11 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
     const float s = P.s;
     const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
     const bool has_draft = !greedy && P.draft != nullptr;
+    // proposals of this sequence (prompt lookup: its own count; invalid counts
+    // stop at once and decide_core reports the sequence invalid)
+    const int Kb = OH ? P.klen[b] : K;
+    const int Ke = OH ? ((Kb >= 0 && Kb <= K) ? Kb : 0) : K;
+    const RowStat d0 = OH ? RowStat{0.f, 1.f, 0, 1} : RowStat{0.f, 0.f, 0, 0};
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ RowStat f_rs[MAXR];
     __shared__ TestIn ti[SV_MAX_K + 1];
@@ -1166,11 +1176,11 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
 
     // rows never streamed stay invalid; the test inputs load while position 0
     // streams (the first barrier below orders both before any read)
-    if (tid < R) f_rs[tid] = {0.f, 0.f, 0, 0};
+    if (tid < R) f_rs[tid] = tid > K ? d0 : RowStat{0.f, 0.f, 0, 0};
     const int tw = (QW - 1) * 64;                  // last wave loads the test inputs
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
 
-    for (int j = 0; j <= K; ++j) {
+    for (int j = 0; j <= Ke; ++j) {
         const char* trow = target_row<DTT>(P, b, j);
         const bool dj = has_draft && j < K;
         if (greedy) {
@@ -1191,7 +1201,7 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
         }
         __syncthreads();
         if (tid == 0) {
-            RowStat t, d = {0.f, 0.f, 0, 0};
+            RowStat t, d = d0;
             if (greedy) {
                 AmState am = sh_a[0];
                 for (int w2 = 1; w2 < QW; ++w2) am = am_merge(am, sh_a[w2]);
@@ -1209,21 +1219,22 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
             }
             f_rs[j] = t;
             bool stop = true;
-            if (j < K) stop = test_from(V, s, greedy, t, d, ti[j].x, ti[j].u, ti[j].lx, ti[j].dx).stop;
+            if (j < Ke) stop = test_from(V, s, greedy, t, d, ti[j].x, ti[j].u, ti[j].lx, ti[j].dx).stop;
             sh_stop = stop;
         }
         __syncthreads();
         if (sh_stop) break;
     }
 
-    decide_core<DTT, DTD>(P, b, greedy, true, true, f_rs, ti, &dec);
+    decide_core<DTT, DTD, OH>(P, b, greedy, true, true, f_rs, ti, &dec);
     if (greedy || !dec.ok) return;                 // uniform across the workgroup
 
     // draw from row n: residual max(0, p - q) scaled by Z_p, or p for the bonus
     const int n = dec.n, nseg = P.nseg;
-    const bool bonus = n == K;
+    const bool bonus = n == Kb;                    // valid sequence: Kb in [0, K]
+    const int32_t ox = (OH && !bonus) ? ti[n].x : -1;   // one-hot draft row at n
     const char* trow = target_row<DTT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const char* drow = (bonus || OH) ? nullptr : draft_row<DTD>(P, b, n);
     const float cp = shift_of(dec.mp, s);
     const float cq = bonus ? 0.f : shift_of(dec.mq, s);
     const float w = bonus ? 0.f : dec.zp / dec.zq;
@@ -1235,7 +1246,10 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
         for (int k = 0; k < QSPW; ++k) {
             const int64_t e = (int64_t)(g0 + k) * SEG + (int64_t)lane * LE;
             load8<DTT>(trow, e, V, t_al, xl[k]);
-            if (!bonus) load8<DTD>(drow, e, V, d_al, xd[k]);
+            if (!bonus) {
+                if constexpr (OH) onehot8(e, ox, xd[k]);
+                else load8<DTD>(drow, e, V, d_al, xd[k]);
+            }
         }
 #pragma unroll
         for (int k = 0; k < QSPW; ++k) {
@@ -1257,7 +1271,7 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
     __syncthreads();
     const Pick pk = find_segment<QT>(seg_r, seg_p, nseg, dec.u, bonus, sh_scan, sh_seg, sh_lo);
     if (wave == 0) {
-        const int y = pk.g >= 0 ? walk_segment<DTT, DTD>(trow, drow, V, pk, s, cp, cq, w) : -1;
+        const int y = pk.g >= 0 ? walk_segment<DTT, DTD>(trow, drow, V, pk, s, cp, cq, w, ox) : -1;
         if (lane == 0) {
             P.out[(int64_t)b * (K + 1) + n] = y;
             put(P.res_mass, b, pk.g < 0 ? NAN : (pk.mode == 2 ? 0.f : pk.S / dec.zp));
@@ -1365,7 +1379,7 @@ __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t e
     }
 }
 
-template <int DTT, int DTD>
+template <int DTT, int DTD, bool OH = false>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_seqg(const Params P)
 {
     const int G = P.G;
@@ -1378,6 +1392,11 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const float s = P.s;
     const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
     const bool has_draft = !greedy && P.draft != nullptr;
+    // proposals of this sequence (prompt lookup: its own count; invalid counts
+    // stop at once and decide_core reports the sequence invalid)
+    const int Kb = OH ? P.klen[b] : K;
+    const int Ke = OH ? ((Kb >= 0 && Kb <= K) ? Kb : 0) : K;
+    const RowStat d0 = OH ? RowStat{0.f, 1.f, 0, 1} : RowStat{0.f, 0.f, 0, 0};
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t salt = P.salt;
     uint64_t* region = P.slots + (int64_t)b * (((int64_t)K + 1) * G * 4 + (int64_t)G * 2);
@@ -1402,12 +1421,12 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
 
     uint32_t ep = 0;
     if (wave == 0) ep = (uint32_t)__hip_atomic_load(P.gep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < R) f_rs[tid] = {0.f, 0.f, 0, 0};
+    if (tid < R) f_rs[tid] = tid > K ? d0 : RowStat{0.f, 0.f, 0, 0};
     const int tw = (GW - 1) * 64;                  // last wave loads the test inputs
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
 
     int jb = 0;                                    // last position streamed
-    for (int j = 0; j <= K; ++j) {
+    for (int j = 0; j <= Ke; ++j) {
         jb = j;
         const char* trow = target_row<DTT>(P, b, j);
         const bool dj = has_draft && j < K;
@@ -1452,7 +1471,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
             }
             // all members' partials, merged in lane order on every member
             bool ok;
-            RowStat t, d = {0.f, 0.f, 0, 0};
+            RowStat t, d = d0;
             const int first = pos_word(K, G, j, lane, 0);
             if (greedy) {
                 uint32_t v[2];
@@ -1484,7 +1503,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                 f_rs[j] = t;
                 if (dj) f_rs[K + 1 + j] = d;
                 bool stop = true;
-                if (j < K) stop = test_from(V, s, greedy, t, d, ti[j].x, ti[j].u, ti[j].lx, ti[j].dx).stop;
+                if (j < Ke) stop = test_from(V, s, greedy, t, d, ti[j].x, ti[j].u, ti[j].lx, ti[j].dx).stop;
                 sh_stop = ok ? (stop ? 1 : 0) : 2;
             }
         }
@@ -1497,14 +1516,15 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         return;
     }
 
-    decide_core<DTT, DTD>(P, b, greedy, g == 0, true, f_rs, ti, &dec);
+    decide_core<DTT, DTD, OH>(P, b, greedy, g == 0, true, f_rs, ti, &dec);
     if (greedy || !dec.ok) return;                 // uniform across the workgroup
 
     // draw from row n: this member's slice of segment sums, then the totals
     const int n = dec.n;
-    const bool bonus = n == K;
+    const bool bonus = n == Kb;                    // valid sequence: Kb in [0, K]
+    const int32_t ox = (OH && !bonus) ? ti[n].x : -1;   // one-hot draft row at n
     const char* trow = target_row<DTT>(P, b, n);
-    const char* drow = bonus ? nullptr : draft_row<DTD>(P, b, n);
+    const char* drow = (bonus || OH) ? nullptr : draft_row<DTD>(P, b, n);
     const float cp = shift_of(dec.mp, s);
     const float cq = bonus ? 0.f : shift_of(dec.mq, s);
     const float w = bonus ? 0.f : dec.zp / dec.zq;
@@ -1516,7 +1536,10 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         for (int k = 0; k < SPW; ++k) {
             const int64_t e = (int64_t)(sg0 + l0 + k) * SEG + (int64_t)lane * LE;
             load8<DTT>(trow, e, V, t_al, xl[k]);
-            if (!bonus) load8<DTD>(drow, e, V, d_al, xd[k]);
+            if (!bonus) {
+                if constexpr (OH) onehot8(e, ox, xd[k]);
+                else load8<DTD>(drow, e, V, d_al, xd[k]);
+            }
         }
 #pragma unroll
         for (int k = 0; k < SPW; ++k) {
@@ -1609,7 +1632,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     pk.thr = sh_pick_thr;
     pk.lo = L.lo;
     if (wave == 0) {
-        const int y = pk.g >= 0 ? walk_segment<DTT, DTD>(trow, drow, V, pk, s, cp, cq, w) : -1;
+        const int y = pk.g >= 0 ? walk_segment<DTT, DTD>(trow, drow, V, pk, s, cp, cq, w, ox) : -1;
         if (lane == 0) {
             P.out[(int64_t)b * (K + 1) + n] = y;
             put(P.res_mass, b, pk.g < 0 ? NAN : (pk.mode == 2 ? 0.f : pk.S / dec.zp));
@@ -1681,7 +1704,7 @@ static int group_max(int32_t B)
 
 // k_seqg workgroups the current device holds at once, per storage-type pair
 // (0 when unknown: the grouped launch is then not used).
-template <int DTT, int DTD>
+template <int DTT, int DTD, bool OH>
 static int group_capacity_t()
 {
     int dev = 0, cus = 0, per_cu = 0;
@@ -1690,7 +1713,7 @@ static int group_capacity_t()
     static std::atomic<bool> init[64];
     if (init[dev].load(std::memory_order_acquire)) return cache[dev].load(std::memory_order_relaxed);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD>), GT,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH>), GT,
                                                      0) != hipSuccess)
         return 0;
     cache[dev].store(cus * per_cu, std::memory_order_relaxed);
@@ -1698,12 +1721,14 @@ static int group_capacity_t()
     return cus * per_cu;
 }
 
-static int group_capacity(int32_t dtt, int32_t dtd)
+static int group_capacity(int32_t dtt, int32_t dtd, bool onehot)
 {
-    if (dtt == SV_BF16 && dtd == SV_BF16) return group_capacity_t<SV_BF16, SV_BF16>();
-    if (dtt == SV_F32 && dtd == SV_F32) return group_capacity_t<SV_F32, SV_F32>();
-    if (dtt == SV_F32 && dtd == SV_BF16) return group_capacity_t<SV_F32, SV_BF16>();
-    return group_capacity_t<SV_BF16, SV_F32>();
+    if (onehot) return dtt == SV_BF16 ? group_capacity_t<SV_BF16, SV_BF16, true>()
+                                      : group_capacity_t<SV_F32, SV_F32, true>();
+    if (dtt == SV_BF16 && dtd == SV_BF16) return group_capacity_t<SV_BF16, SV_BF16, false>();
+    if (dtt == SV_F32 && dtd == SV_F32) return group_capacity_t<SV_F32, SV_F32, false>();
+    if (dtt == SV_F32 && dtd == SV_BF16) return group_capacity_t<SV_F32, SV_BF16, false>();
+    return group_capacity_t<SV_BF16, SV_F32, false>();
 }
 
 // Automatic choice.  The per-sequence schedule (one launch, no row past a
@@ -1713,9 +1738,16 @@ static int group_capacity(int32_t dtt, int32_t dtd)
 // which pays one latency-bound launch per position (5-20 us each on
 // gfx950), wins once the eager stream is long against K+1 such launches: at
 // least 64 MiB of logits per position; else eager.
-static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd)
+static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd, bool onehot = false)
 {
     const int m = mode_now();
+    if (onehot) {                                  // no draft rows; lazy launches do not take one-hot rows
+        const double bt = dtt == SV_BF16 ? 2 : 4;
+        const bool seq_ok = nseg_of(V) <= QMAXSEG;
+        if (m == SV_MODE_SEQ) return seq_ok ? SEQ : EAGER;
+        if (m == SV_MODE_EAGER || m == SV_MODE_LAZY) return EAGER;
+        return (seq_ok && (double)B * V * bt >= 64.0 * (1 << 20)) ? SEQ : EAGER;
+    }
     const bool seq_ok = nseg_of(V) <= QMAXSEG;
     if (m == SV_MODE_SEQ) return seq_ok ? SEQ : (K == 0 ? EAGER : LAZY);
     if (m == SV_MODE_EAGER) return EAGER;
@@ -1784,7 +1816,7 @@ static size_t dtype_bytes(int32_t dt) { return dt == SV_BF16 ? 2 : 4; }
 static int prepare(const void* target, const void* draft, const int32_t* tokens, const float* uniforms,
                    float T, const uint8_t* greedy, int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd,
                    int32_t* acc, int32_t* out, const sv_diag* diag, void* ws, size_t ws_bytes,
-                   Params* P, Plan* pl, int force = -1)
+                   Params* P, Plan* pl, int force = -1, bool onehot = false)
 {
     (void)greedy;
     if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
@@ -1838,11 +1870,11 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->gsegs = pl->nseg;
     P->salt = 0;
     P->klen = nullptr;
-    P->onehot = 0;
+    P->onehot = onehot ? 1 : 0;
     if (pl->sched == SEQ) {
         // as many workgroups per sequence as fit on the device at once (each
         // waits for the others), within the workspace's and LDS's limits
-        int64_t G = group_capacity(dtt, dtd) / group_slots(B);
+        int64_t G = group_capacity(dtt, dtd, onehot) / group_slots(B);
         if (G > pl->gmax) G = pl->gmax;
         const int lim = groups_now();
         if (lim > 0 && G > lim) G = lim;
@@ -1867,10 +1899,17 @@ template <int DTT, int DTD>
 static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
 {
     if (pl.sched == SEQ) {                         // the whole step in one launch
-        if (pl.G >= 2)
-            hipLaunchKernelGGL((k_seqg<DTT, DTD>), dim3((unsigned)(group_slots(P.B) * pl.G)), dim3(GT), 0, st, P);
-        else
+        const dim3 gg((unsigned)(group_slots(P.B) * pl.G));
+        if (P.onehot) {                            // one storage type: no draft logits
+            if constexpr (DTT == DTD) {
+                if (pl.G >= 2) hipLaunchKernelGGL((k_seqg<DTT, DTT, true>), gg, dim3(GT), 0, st, P);
+                else hipLaunchKernelGGL((k_seq<DTT, DTT, true>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
+            }
+        } else if (pl.G >= 2) {
+            hipLaunchKernelGGL((k_seqg<DTT, DTD>), gg, dim3(GT), 0, st, P);
+        } else {
             hipLaunchKernelGGL((k_seq<DTT, DTD>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
+        }
         return;
     }
     if (!pl.lazy) {
@@ -2021,16 +2060,17 @@ int spec_verify_lookup(const void* target_logits, int32_t dtype, const int32_t* 
                        int32_t V, int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag, void* workspace,
                        size_t workspace_bytes, void* stream)
 {
-    // the eager launches with one-hot draft rows that are never stored and
-    // target rows past each sequence's proposals skipped
+    // one-hot draft rows that are never stored; target rows past each
+    // sequence's proposals are never read.  Eager, or per-sequence when the
+    // mode (or the automatic rule on the target rows alone) picks it
     sv::Params P;
     sv::Plan pl;
     if (B > 0 && (!klen || (reinterpret_cast<uintptr_t>(klen) & 3u))) return SV_EINVAL;
     int rc = sv::prepare(target_logits, nullptr, cand, uniforms, temperature, greedy_flag, B, K, V, dtype, dtype,
-                         accepted_len, out_tokens, diag, workspace, workspace_bytes, &P, &pl, sv::EAGER);
+                         accepted_len, out_tokens, diag, workspace, workspace_bytes, &P, &pl,
+                         sv::choose_sched(B, K, V, dtype, dtype, true), true);
     if (rc <= 0) return rc;
     P.klen = klen;
-    P.onehot = 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
     rc = sv::launch_stats(P, pl, dtype, dtype, st);
     if (rc != SV_OK) return rc;

@@ -87,9 +87,27 @@ def _as_workload(lw, cand):
                       lw.uniforms, lw.greedy)
 
 
+@pytest.fixture
+def schedule(dev, request):
+    mode, groups = request.param
+    binding.set_mode(mode)
+    binding.set_seq_groups(groups)
+    yield request.param
+    binding.set_mode(binding.MODE_AUTO)
+    binding.set_seq_groups(0)
+
+
+# eager, per-sequence with as many members as fit, per-sequence with one
+# 1024-thread workgroup (lazy maps to eager for one-hot proposals)
+SCHED = pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1),
+                                             (binding.MODE_LAZY, 0)],
+                                indirect=True, ids=["eager", "seq", "seq1", "lazy"])
+
+
+@SCHED
 @pytest.mark.parametrize("B,K,V,Lmax,dtype,greedy_every", [(48, 8, 32000, 512, I.F32, 0), (64, 6, 50001, 600, I.BF16, 3),
                                                            (16, 4, 4097, 100, I.BF16, 0), (9, 0, 1000, 50, I.F32, 0)])
-def test_verify_lookup_matches_oracle(dev, B, K, V, Lmax, dtype, greedy_every):
+def test_verify_lookup_matches_oracle(dev, schedule, B, K, V, Lmax, dtype, greedy_every):
     mask = np.zeros(B, np.uint8) if not greedy_every else (np.arange(B) % greedy_every == 0).astype(np.uint8)
     lw = I.synth_lookup(21 + B + K, B, K, V, Lmax, dtype=dtype, T=0.9, greedy_mask=mask, name=f"lookup_{B}_{K}_{V}")
     cand, klen = lookup.propose(lw.history, lw.hist_len, lw.n_max, lw.n_min, K)
@@ -102,7 +120,9 @@ def test_verify_lookup_matches_oracle(dev, B, K, V, Lmax, dtype, greedy_every):
     assert g["accepted_len"][1] == -1 if B > 2 else True
 
 
-def test_propose_then_verify_full_size(dev):
+@pytest.mark.parametrize("schedule", [(binding.MODE_AUTO, 0), (binding.MODE_EAGER, 0), (binding.MODE_SEQ, 1)],
+                         indirect=True, ids=["auto", "eager", "seq1"])
+def test_propose_then_verify_full_size(dev, schedule):
     """B=256 histories of 2-4k tokens, V=152064 bf16: the GPU proposer feeds the
     GPU verify step; checked against the oracle chain on 32 sampled sequences."""
     import torch
@@ -127,7 +147,9 @@ def test_propose_then_verify_full_size(dev):
          f"{np.bincount(g['accepted_len'][g['accepted_len'] >= 0], minlength=lw.K + 1).tolist()}")
 
 
-def test_onehot_law_chi_square(dev):
+@pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.MODE_SEQ, 0)], indirect=True,
+                         ids=["eager", "seq"])
+def test_onehot_law_chi_square(dev, schedule):
     """10^6 trials on one 32-token row with a one-hot proposal: the first emitted
     token follows p_0 (accept with p_0(x), else p_0 without x)."""
     import torch

@@ -111,3 +111,33 @@ def test_kv_commit_host_checks(lib, kw):
 
 def test_kv_commit_empty_batch(lib):
     assert lib.sv_kv_commit(None, None, None, None, 1, 0, 4, 1, 10, 16, None, None) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(Lmax=-1), dict(n_min=0), dict(n_max=1, n_min=2), dict(n_max=65),
+                                dict(K=-1), dict(K=64), dict(hist_len=None), dict(klen=None), dict(cand=None),
+                                dict(history=None), dict(hist_len=FAKE + 2), dict(cand=FAKE + 1)])
+def test_lookup_propose_host_checks(lib, kw):
+    a = dict(history=FAKE, hist_len=FAKE, B=3, Lmax=50, n_max=4, n_min=1, K=5, cand=FAKE, klen=FAKE)
+    a.update(kw)
+    assert lib.sv_lookup_propose(a["history"], a["hist_len"], a["B"], a["Lmax"], a["n_max"], a["n_min"], a["K"],
+                                 a["cand"], a["klen"], None) == -1
+
+
+def test_lookup_propose_empty_batch(lib):
+    assert lib.sv_lookup_propose(None, None, 0, 10, 4, 1, 5, None, None, None) == 0
+
+
+def test_verify_lookup_host_checks(lib):
+    import ctypes as C
+    ws = 1 << 26
+    args = lambda **kw: [kw.get("target", FAKE), kw.get("dt", 1), kw.get("cand", FAKE), kw.get("klen", FAKE), FAKE,
+                         C.c_float(kw.get("T", 1.0)), None, kw.get("B", 4), kw.get("K", 3), kw.get("V", 100), FAKE,
+                         FAKE, None, FAKE, kw.get("ws", ws), None]
+    assert lib.spec_verify_lookup(*args(klen=None)) == -1
+    assert lib.spec_verify_lookup(*args(klen=FAKE + 2)) == -1
+    assert lib.spec_verify_lookup(*args(cand=None)) == -1
+    assert lib.spec_verify_lookup(*args(dt=3)) == -1
+    assert lib.spec_verify_lookup(*args(T=0.0)) == -1
+    assert lib.spec_verify_lookup(*args(K=64)) == -1
+    assert lib.spec_verify_lookup(*args(ws=16)) == -2
+    assert lib.spec_verify_lookup(*args(B=0, klen=None)) == 0
