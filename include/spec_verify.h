@@ -286,6 +286,12 @@ int sv_schedule(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t d
 int sv_set_seq_groups(int groups);
 int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
 
+/* The HIP error code (hipError_t) behind this thread's most recent
+ * SV_ELAUNCH, 0 if none yet.  Entry points clear an error left by an earlier
+ * HIP call of the caller before launching, so SV_ELAUNCH always means one of
+ * this library's launches failed.                                          */
+int sv_last_hip_error(void);
+
 /* Short text for a return code (static storage). */
 const char* sv_strerror(int code);
 

@@ -24,7 +24,7 @@ SV_MAX_K = 63
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups",
-           "sv_lookup_propose", "spec_verify_lookup",
+           "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
            "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
 
@@ -36,8 +36,12 @@ class SvDiag(C.Structure):
 
 class SpecVerifyError(RuntimeError):
     def __init__(self, code: int, msg: str):
-        super().__init__(f"{msg} (code {code})")
+        hip = None
+        if code == SV_ELAUNCH and _lib is not None:
+            hip = int(_lib.sv_last_hip_error())
+        super().__init__(f"{msg} (code {code}" + (f", hipError_t {hip})" if hip is not None else ")"))
         self.code = code
+        self.hip_error = hip
 
 
 _lib = None
@@ -45,10 +49,19 @@ _lock = threading.Lock()
 
 
 def load_library(path: str = LIB_PATH):
-    """Load the HIP library (no GPU needed to load it)."""
+    """Load the HIP library (no GPU needed to load it).
+
+    PyTorch-ROCm brings its own HIP runtime under the same soname; loaded
+    first, ours would pull a second runtime into the process, which then sees
+    no device.  So torch, when installed, is imported before the library, and
+    the library binds to the runtime torch already loaded."""
     global _lib
     with _lock:
         if _lib is None:
+            try:
+                import torch  # noqa: F401  (one HIP runtime per process)
+            except ImportError:
+                pass
             if not os.path.exists(path):
                 raise RuntimeError(
                     f"{path} is missing: build it with "
@@ -77,6 +90,8 @@ def load_library(path: str = LIB_PATH):
             lib.sv_kv_commit.restype = C.c_int
             lib.sv_kv_commit.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+            lib.sv_last_hip_error.restype = C.c_int
+            lib.sv_last_hip_error.argtypes = []
             lib.sv_lookup_propose.restype = C.c_int
             lib.sv_lookup_propose.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 5 + [C.c_void_p] * 3
             lib.spec_verify_lookup.restype = C.c_int

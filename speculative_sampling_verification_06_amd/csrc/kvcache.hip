@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include "spec_verify.h"
+#include "sv_internal.h"
 
 namespace svkv {
 
@@ -121,11 +122,12 @@ int sv_kv_commit(void* cache, int32_t* cache_len, const void* staged, const int3
     P.chunks = (int32_t)chunks;
     P.vec = row_bytes % 16 == 0 && svkv::aligned_to(cache, 16) && (!staged || svkv::aligned_to(staged, 16));
     hipStream_t st = static_cast<hipStream_t>(stream);
+    sv_launch_begin();
     if (staged)
         hipLaunchKernelGGL(svkv::k_kv_copy, dim3((unsigned)((int64_t)planes * B * chunks)), dim3(svkv::NT), 0, st, P);
     hipLaunchKernelGGL(svkv::k_kv_len, dim3((unsigned)((B + svkv::NT - 1) / svkv::NT)), dim3(svkv::NT), 0, st, P,
                        cache_len, status);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    return sv_launch_status();
 }
 
 }  // extern "C"

@@ -225,9 +225,10 @@ int sv_lmhead_pack(const void* w_dv, void* w_vd, int32_t d, int32_t V, void* str
     if (!svlm::aligned_to(w_dv, 2) || !svlm::aligned_to(w_vd, 2)) return SV_EINVAL;
     if ((d + 63) / 64 > 65535) return SV_EINVAL;
     const dim3 grid((unsigned)((V + 63) / 64), (unsigned)((d + 63) / 64));
+    sv_launch_begin();
     hipLaunchKernelGGL(svlm::k_pack, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint16_t*>(w_dv), static_cast<uint16_t*>(w_vd), d, V);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    return sv_launch_status();
 }
 
 int sv_lmhead(const void* hidden, const void* w_vd, int32_t M, int32_t d, int32_t V, float* logits,
@@ -236,9 +237,10 @@ int sv_lmhead(const void* hidden, const void* w_vd, int32_t M, int32_t d, int32_
     const int rc = svlm::check_gemm(hidden, w_vd, M, d, V, logits);
     if (rc <= 0) return rc;
     const dim3 grid((unsigned)((V + svlm::BN - 1) / svlm::BN), (unsigned)((M + svlm::MB - 1) / svlm::MB));
+    sv_launch_begin();
     hipLaunchKernelGGL(svlm::k_lmhead, grid, dim3(svlm::NT), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_vd), logits, M, d, V);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    return sv_launch_status();
 }
 
 int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* target_logits,

@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include "spec_verify.h"
+#include "sv_internal.h"
 
 namespace svpl {
 
@@ -117,8 +118,9 @@ int sv_lookup_propose(const int32_t* history, const int32_t* hist_len, int32_t B
     P.n_max = n_max;
     P.n_min = n_min;
     P.K = K;
+    sv_launch_begin();
     hipLaunchKernelGGL(svpl::k_lookup, dim3((unsigned)B), dim3(svpl::NT), 0, static_cast<hipStream_t>(stream), P);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    return sv_launch_status();
 }
 
 }  // extern "C"

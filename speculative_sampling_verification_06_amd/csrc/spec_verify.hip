@@ -1306,6 +1306,7 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
 constexpr int GT = 256;               // threads per workgroup
 constexpr int GW = GT / 64;
 constexpr int GU = 2;                 // 16-byte loads in flight per lane and row
+constexpr int GSPW = 4;               // draw: segments per wave per step
 constexpr int GMAXG = 64;             // members per sequence at most (one wave gathers them)
 constexpr int GMAXSEG = 2048;         // segment sums of one slice held in LDS
 constexpr int GCAP = 4096;            // workgroups per launch at most (workspace sizing)
@@ -1530,10 +1531,10 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const float w = bonus ? 0.f : dec.zp / dec.zq;
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
-    for (int l0 = wave * SPW; l0 < nl; l0 += GW * SPW) {
-        float xl[SPW][LE], xd[SPW][LE];
+    for (int l0 = wave * GSPW; l0 < nl; l0 += GW * GSPW) {
+        float xl[GSPW][LE], xd[GSPW][LE];
 #pragma unroll
-        for (int k = 0; k < SPW; ++k) {
+        for (int k = 0; k < GSPW; ++k) {
             const int64_t e = (int64_t)(sg0 + l0 + k) * SEG + (int64_t)lane * LE;
             load8<DTT>(trow, e, V, t_al, xl[k]);
             if (!bonus) {
@@ -1542,7 +1543,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
             }
         }
 #pragma unroll
-        for (int k = 0; k < SPW; ++k) {
+        for (int k = 0; k < GSPW; ++k) {
             float sr = 0.f, sp = 0.f;
 #pragma unroll
             for (int qq = 0; qq < LE; ++qq) {
@@ -1708,14 +1709,19 @@ template <int DTT, int DTD, bool OH>
 static int group_capacity_t()
 {
     int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
     static std::atomic<int> cache[64];
     static std::atomic<bool> init[64];
     if (init[dev].load(std::memory_order_acquire)) return cache[dev].load(std::memory_order_relaxed);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH>), GT,
-                                                     0) != hipSuccess)
+                                                     0) != hipSuccess) {
+        (void)hipGetLastError();                   // unknown capacity: one workgroup per sequence
         return 0;
+    }
     cache[dev].store(cus * per_cu, std::memory_order_relaxed);
     init[dev].store(true, std::memory_order_release);
     return cus * per_cu;
@@ -1942,17 +1948,31 @@ static void launch_draw_t(const Params& P, const Plan& pl, hipStream_t st)
 
 static int launch_stats(const Params& P, const Plan& pl, int32_t dtt, int32_t dtd, hipStream_t st)
 {
+    sv_launch_begin();
     SV_DISPATCH(launch_rowstats_t, dtt, dtd, P, pl, st);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    return sv_launch_status();
 }
 
 static int launch_draw(const Params& P, const Plan& pl, int32_t dtt, int32_t dtd, hipStream_t st)
 {
+    sv_launch_begin();
     SV_DISPATCH(launch_draw_t, dtt, dtd, P, pl, st);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ELAUNCH;
+    return sv_launch_status();
 }
 
 }  // namespace sv
+
+static thread_local int g_last_hip = 0;
+
+void sv_launch_begin(void) { (void)hipGetLastError(); }
+
+int sv_launch_status(void)
+{
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return SV_OK;
+    g_last_hip = (int)e;
+    return SV_ELAUNCH;
+}
 
 // Verify step with separate storage types for target and draft logits (the
 // fused LM-head path feeds fp32 target logits and bf16 draft logits).
@@ -2085,6 +2105,8 @@ int sv_set_mode(int mode)
 }
 
 int sv_get_mode(void) { return sv::mode_now(); }
+
+int sv_last_hip_error(void) { return g_last_hip; }
 
 int sv_set_seq_groups(int groups)
 {

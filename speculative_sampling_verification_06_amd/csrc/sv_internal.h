@@ -15,4 +15,11 @@ int sv_verify_mixed(const void* target, const void* draft, const int32_t* tokens
                     int32_t dtd, int32_t* acc, int32_t* out, const sv_diag* diag, void* ws,
                     size_t ws_bytes, void* stream, int check_only);
 
+// Launch bookkeeping of every entry point: sv_launch_begin() clears an error a
+// caller's earlier HIP call may have left (it is not this call's failure);
+// sv_launch_status() after the launches returns SV_OK or SV_ELAUNCH and keeps
+// the HIP error code for sv_last_hip_error().
+void sv_launch_begin(void);
+int sv_launch_status(void);
+
 #endif
