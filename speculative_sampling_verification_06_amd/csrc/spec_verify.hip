@@ -1305,8 +1305,8 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
 
 constexpr int GT = 256;               // threads per workgroup
 constexpr int GW = GT / 64;
-constexpr int GU = 2;                 // 16-byte loads in flight per lane and row
-constexpr int GSPW = 4;               // draw: segments per wave per step
+constexpr int GU = 3;                 // 16-byte loads in flight per lane and row
+constexpr int GSPW = 2;               // draw: segments per wave per step
 constexpr int GMAXG = 64;             // members per sequence at most (one wave gathers them)
 constexpr int GMAXSEG = 2048;         // segment sums of one slice held in LDS
 constexpr int GCAP = 4096;            // workgroups per launch at most (workspace sizing)
