@@ -109,6 +109,19 @@ SCHEDULES = {1: "eager (one launch streams every row)",
              3: "seq (one workgroup per sequence walks its positions, reached rows only, draws in place)"}
 
 
+def _copy_calibration(args, torch, dev):
+    """A device copy of known size for scaling the traffic counters (profiler runs)."""
+    if args.copy_calibration_mib <= 0:
+        return
+    n = args.copy_calibration_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def bench_verify(args, torch, np, binding, I, dev):
     w = I.CONFIGS[args.config]()
     print(f"[bench] workload {w.name}: generated", file=sys.stderr, flush=True)
@@ -117,14 +130,7 @@ def bench_verify(args, torch, np, binding, I, dev):
     call = binding.Bound(*a)                       # checks, outputs and workspace, once
     out = call.verify()
     stream = torch.cuda.current_stream(dev)
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr, flush=True)
-        del src, dst
+    _copy_calibration(args, torch, dev)
     for _ in range(args.warmup):
         call.stats()
         call.draw()
@@ -183,6 +189,7 @@ def bench_lmhead(args, torch, np, binding, I, dev):
     call = binding.Bound(logits, dd["draft"], dd["tokens"], dd["uniforms"], w.T, dd["greedy"])
     out = call.verify()
     stream = torch.cuda.current_stream(dev)
+    _copy_calibration(args, torch, dev)
     for _ in range(args.warmup):
         gemm()
         call.verify()

@@ -155,22 +155,31 @@ int sv_draw(const void* target_logits, const void* draft_logits,
  *     target_logits[m, v] = sum_k hidden[m, k] * W[k, v]   (m < B*(K+1)),
  * bf16 inputs, fp32 accumulation and output.
  *
+ * sv_lmhead_packed_bytes: bytes of the packed weight for W [d, V]:
+ *   ceil(V/256) * 8 * ceil(d/16) * 1024; 0 when d < 1 or V < 1.
  * sv_lmhead_pack: one-time repack of the static weight from W [d, V] (bf16,
- *   row-major) into w_vd = W^T [V, d] (the [out_features, in_features]
- *   layout), which the GEMM streams.  Both caller-owned device buffers.
- *   EINVAL on d < 1, V < 1, NULL or misaligned (2 B) pointers.
- * sv_lmhead: logits [M, V] fp32 = hidden [M, d] bf16 x W with w_vd [V, d]
- *   bf16.  d must be a multiple of 8 and hidden / w_vd 16-byte aligned
- *   (EINVAL otherwise); M == 0 is a no-op.
+ *   row-major) into w_packed, the matrix-core operand tiles the GEMM streams:
+ *   with KT = ceil(d/16), tile (vt, kt), vt < ceil(V/32), kt < KT, is 1 KB at
+ *   offset ((vt/8 * KT + kt) * 8 + vt%8) * 1024 bytes (the 8 tiles of each
+ *   256 columns alternate per k-tile); its bf16 element l*8 + e (l < 64,
+ *   e < 8) is W[kt*16 + 8*(l/32) + e][vt*32 + l%32], 0 past d or V.  Tiles
+ *   past ceil(V/32) in the last group are not written.
+ *   Both caller-owned device buffers, w_packed of sv_lmhead_packed_bytes.
+ *   EINVAL on d < 1, V < 1, NULL pointers, w_dv not 2-byte or w_packed not
+ *   16-byte aligned.
+ * sv_lmhead: logits [M, V] fp32 = hidden [M, d] bf16 x W, W given as
+ *   w_packed.  d must be a multiple of 8 and hidden / w_packed 16-byte
+ *   aligned (EINVAL otherwise); M == 0 is a no-op.
  * spec_lmhead_verify: sv_lmhead on hidden [B, K+1, d] into the caller's
  *   target_logits [B, K+1, V] fp32 buffer, then the verify step of
  *   spec_verify on those logits with draft logits of draft_dtype.  Every
  *   check of both parts runs before anything is launched; outputs, errors
  *   and workspace as spec_verify (size it with dtype SV_F32).            */
-int sv_lmhead_pack(const void* w_dv, void* w_vd, int32_t d, int32_t V, void* stream);
-int sv_lmhead(const void* hidden, const void* w_vd, int32_t M, int32_t d, int32_t V,
+size_t sv_lmhead_packed_bytes(int32_t d, int32_t V);
+int sv_lmhead_pack(const void* w_dv, void* w_packed, int32_t d, int32_t V, void* stream);
+int sv_lmhead(const void* hidden, const void* w_packed, int32_t M, int32_t d, int32_t V,
               float* logits, void* stream);
-int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* target_logits,
+int spec_lmhead_verify(const void* hidden, const void* w_packed, int32_t d, float* target_logits,
                        const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
                        const float* uniforms, float temperature, const uint8_t* greedy_flag,
                        int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,

@@ -21,7 +21,7 @@ SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_ELAUNCH = 0, -1, -2, -3
 SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
-EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_pack", "sv_lmhead",
+EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_packed_bytes", "sv_lmhead_pack", "sv_lmhead",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups",
            "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
@@ -109,6 +109,8 @@ def load_library(path: str = LIB_PATH):
             lib.sv_set_seq_groups.argtypes = [C.c_int]
             lib.sv_seq_groups.restype = C.c_int
             lib.sv_seq_groups.argtypes = [C.c_int32] * 5
+            lib.sv_lmhead_packed_bytes.restype = C.c_size_t
+            lib.sv_lmhead_packed_bytes.argtypes = [C.c_int32, C.c_int32]
             lib.sv_lmhead_pack.restype = C.c_int
             lib.sv_lmhead_pack.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
             lib.sv_lmhead.restype = C.c_int
@@ -379,18 +381,18 @@ class Bound:
 class BoundLMHead:
     """The LM-head GEMM of one problem with pre-marshalled arguments."""
 
-    def __init__(self, hidden2d, w_vd, logits2d, stream=None):
+    def __init__(self, hidden2d, packed, logits2d, stream=None):
         torch = _torch()
         M, d = hidden2d.shape
-        V = w_vd.shape[0]
+        V = packed.V
         _dev_ptr(hidden2d, "hidden", torch.bfloat16, (M, d))
-        _dev_ptr(w_vd, "w_vd", torch.bfloat16, (V, d))
+        _check_packed(packed, d)
         _dev_ptr(logits2d, "logits", torch.float32, (M, V))
         if stream is None:
             stream = torch.cuda.current_stream(hidden2d.device).cuda_stream
-        self._keep = (hidden2d, w_vd, logits2d)
+        self._keep = (hidden2d, packed, logits2d)
         self._fn = load_library().sv_lmhead
-        self._args = (C.c_void_p(hidden2d.data_ptr()), C.c_void_p(w_vd.data_ptr()), C.c_int32(M), C.c_int32(d),
+        self._args = (C.c_void_p(hidden2d.data_ptr()), C.c_void_p(packed.data.data_ptr()), C.c_int32(M), C.c_int32(d),
                       C.c_int32(V), C.c_void_p(logits2d.data_ptr()), C.c_void_p(stream))
 
     def __call__(self):
@@ -404,35 +406,59 @@ def _check_rc(rc):
         raise SpecVerifyError(rc, strerror(rc))
 
 
+class PackedWeight:
+    """The LM-head weight W [d, V] in the GEMM's tiled layout (sv_lmhead_pack):
+    `data` is a 1-D bf16 device tensor of sv_lmhead_packed_bytes(d, V) bytes."""
+
+    def __init__(self, data, d, V):
+        self.data, self.d, self.V = data, int(d), int(V)
+
+
+def packed_bytes(d, V):
+    """sv_lmhead_packed_bytes: size of the tiled weight for W [d, V] (0 if d or V < 1)."""
+    return int(load_library().sv_lmhead_packed_bytes(d, V))
+
+
+def _check_packed(packed, d):
+    torch = _torch()
+    if not isinstance(packed, PackedWeight):
+        raise TypeError("the LM-head weight must be the PackedWeight that lmhead_pack returns")
+    if packed.d != d:
+        raise ValueError(f"hidden size {d} does not match the packed weight's {packed.d}")
+    _dev_ptr(packed.data, "packed weight", torch.bfloat16, (packed_bytes(packed.d, packed.V) // 2,))
+
+
 def lmhead_pack(w_dv, out=None):
-    """One-time repack of the static LM-head weight W [d, V] bf16 into W^T [V, d]."""
+    """One-time repack of the static LM-head weight W [d, V] bf16 into the
+    GEMM's tiled layout; returns a PackedWeight (its data in `out` if given)."""
     torch = _torch()
     d, V = w_dv.shape
     _dev_ptr(w_dv, "w_dv", torch.bfloat16, (d, V))
+    n = packed_bytes(d, V) // 2
     if out is None:
-        out = torch.empty(V, d, dtype=torch.bfloat16, device=w_dv.device)
-    _dev_ptr(out, "w_vd", torch.bfloat16, (V, d))
+        out = torch.empty(n, dtype=torch.bfloat16, device=w_dv.device)
+    _dev_ptr(out, "packed weight", torch.bfloat16, (n,))
     _check_rc(load_library().sv_lmhead_pack(w_dv.data_ptr(), out.data_ptr(), d, V,
                                             torch.cuda.current_stream(w_dv.device).cuda_stream))
-    return out
+    return PackedWeight(out, d, V)
 
 
-def lmhead(hidden, w_vd, out=None):
-    """logits [M, V] fp32 = hidden [M, d] bf16 x W, with w_vd = W^T [V, d] bf16."""
+def lmhead(hidden, packed, out=None):
+    """logits [M, V] fp32 = hidden [M, d] bf16 x W, W given packed (lmhead_pack)."""
     torch = _torch()
     M, d = hidden.shape
-    V = w_vd.shape[0]
+    V = packed.V
     _dev_ptr(hidden, "hidden", torch.bfloat16, (M, d))
-    _dev_ptr(w_vd, "w_vd", torch.bfloat16, (V, d))
+    _check_packed(packed, d)
     if out is None:
         out = torch.empty(M, V, dtype=torch.float32, device=hidden.device)
     _dev_ptr(out, "logits", torch.float32, (M, V))
-    _check_rc(load_library().sv_lmhead(hidden.data_ptr(), w_vd.data_ptr(), M, d, V, out.data_ptr(),
+    _check_rc(load_library().sv_lmhead(hidden.data_ptr(), packed.data.data_ptr(), M, d, V, out.data_ptr(),
                                        torch.cuda.current_stream(hidden.device).cuda_stream))
     return out
 
 
-def lmhead_verify(hidden, w_vd, draft, tokens, uniforms, temperature, greedy=None, *,
+def lmhead_verify(hidden, packed, draft, tokens, uniforms, temperature, greedy=None, *,
                   target_logits=None, diag=True, stream=None):
     """spec_lmhead_verify: the LM-head GEMM into target_logits [B, K+1, V] fp32,
     then the verify step.  Returns Outputs (+ target_logits)."""
@@ -440,10 +466,10 @@ def lmhead_verify(hidden, w_vd, draft, tokens, uniforms, temperature, greedy=Non
     lib = load_library()
     B, K1, d = hidden.shape
     K = K1 - 1
-    V = w_vd.shape[0]
+    V = packed.V
     dev = hidden.device
     _dev_ptr(hidden, "hidden", torch.bfloat16, (B, K + 1, d))
-    _dev_ptr(w_vd, "w_vd", torch.bfloat16, (V, d))
+    _check_packed(packed, d)
     if draft is not None:
         _dev_ptr(draft, "draft_logits", shape=(B, K, V))
     if target_logits is None:
@@ -465,7 +491,7 @@ def lmhead_verify(hidden, w_vd, draft, tokens, uniforms, temperature, greedy=Non
         stream = torch.cuda.current_stream(dev).cuda_stream
     ddt = SV_F32 if draft is None else _dtype_code(draft)
     _check_rc(lib.spec_lmhead_verify(
-        hidden.data_ptr(), w_vd.data_ptr(), d, target_logits.data_ptr(),
+        hidden.data_ptr(), packed.data.data_ptr(), d, target_logits.data_ptr(),
         None if draft is None else draft.data_ptr(), ddt,
         None if tokens is None or tokens.numel() == 0 else tokens.data_ptr(), uniforms.data_ptr(),
         C.c_float(float(temperature)), None if greedy is None else greedy.data_ptr(), B, K, V,

@@ -9,13 +9,19 @@
 // workload).  At M = 192 it does 2*M flops per weight element: HBM-bound on
 // streaming W once (1.05 GB), with MFMA needed at about half its peak.
 //
-// Layout: W is static, so it is packed once (k_pack) from [d, V] into
-// Wt = W^T [V, d] (the usual [out_features, in_features] weight layout), which
-// makes both MFMA operands contiguous along k.  k_lmhead: one workgroup = 4
-// waves; each wave owns 64 vocabulary rows of Wt (two 32-wide MFMA tiles) and
-// all 192 hidden rows (six 32-row tiles) of an M block, so every Wt element
-// is read from HBM exactly once and each 16-k step issues 12
-// v_mfma_f32_32x32x16_bf16.  Wt fragments stream into a register ring two
+// Layout: W is static, so it is packed once (k_pack) from [d, V] into MFMA
+// operand tiles: tile (vt, kt) holds the 32 vocabulary columns vt*32.. and the
+// 16 k values kt*16.. of W as 64 lanes x 8 bf16 in the B-operand lane order
+// below (1 KB), zero past V and past d; the 8 tiles of one workgroup's 256
+// columns alternate per k-tile (tile_off).  Each wave load of a weight
+// fragment is one contiguous kilobyte and a workgroup's k-step reads one
+// contiguous 8 KB, where reading 32 rows of W^T 32 bytes at a time left DRAM
+// rows half used (351 -> 271 us for the workload above).  k_lmhead: one
+// workgroup = 4 waves, one per SIMD; each wave owns two vocabulary tiles (64
+// columns) and all 192 hidden rows (six 32-row tiles) of an M block, so every
+// W element is read from HBM exactly once and each 16-k step issues 12
+// v_mfma_f32_32x32x16_bf16 on one A fragment per tile pair (the 192
+// accumulators sit in AGPRs).  Weight tiles stream into a register ring RB
 // 64-k blocks deep; the hidden states (1.5 MB, L2-resident) come through a
 // double-buffered LDS block shared by the four waves, the next block's loads
 // in flight while the current one is multiplied.
@@ -40,10 +46,36 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int NT = 256;           // four wave64
-constexpr int WN = 64;            // vocabulary rows per wave
+constexpr int NC = 2;             // 32-wide vocabulary tiles per wave
+constexpr int WN = 32 * NC;       // vocabulary rows per wave
+constexpr int WPS = 1;            // waves per SIMD the register budget allows
 constexpr int BN = 4 * WN;        // per workgroup
 constexpr int MT = 6;             // 32-row tiles per M block
 constexpr int MB = 32 * MT;       // 192 hidden rows per M block
+constexpr int TG = BN / 32;       // vocabulary tiles interleaved per k-tile in the packed weight
+
+// Element offset of packed tile (vt, kt) for KT k-tiles: the TG tiles of one
+// workgroup alternate per k-tile, so its four waves read one contiguous
+// TG KB per k-step.
+__host__ __device__ __forceinline__ int64_t tile_off(int vt, int kt, int KT)
+{
+    return (((int64_t)(vt / TG) * KT + kt) * TG + vt % TG) * 512;
+}
+
+// Barrier for the LDS hand-over only: this wave's LDS stores complete
+// (lgkmcnt 0), then s_barrier.  __syncthreads() would also wait for every
+// outstanding global load (vmcnt 0), draining the weight prefetch ring each
+// block.  The signal fences keep the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);    // gfx9 encoding: lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p)
 {
@@ -51,21 +83,25 @@ __device__ __forceinline__ bf16x8 ld16(const uint16_t* p)
     return __builtin_bit_cast(bf16x8, v);
 }
 
-__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wt,
-                                              int d, int V)
+// Packed offset of element (lane l, e) of tile (vt, kt): ((vt * KT + kt) * 64
+// + l) * 8 + e, holding W[kt*16 + 8*(l/32) + e][vt*32 + l%32] (0 outside).
+// One workgroup per (vocabulary tile, 64 k): W[k0..k0+63][v0..v0+31] through
+// LDS, then four tiles written contiguously.
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, uint16_t* __restrict__ P,
+                                              int d, int V, int KT)
 {
-    __shared__ uint16_t tile[64][66];
-    const int k0 = blockIdx.y * 64, v0 = blockIdx.x * 64;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int r = i >> 6, c = i & 63;
+    __shared__ uint16_t tile[64][34];
+    const int vt = blockIdx.x, k0 = blockIdx.y * 64, v0 = vt * 32;
+    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+        const int r = i >> 5, c = i & 31;
         const int k = k0 + r, v = v0 + c;
         tile[r][c] = (k < d && v < V) ? W[(int64_t)k * V + v] : (uint16_t)0;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int r = i >> 6, c = i & 63;
-        const int v = v0 + r, k = k0 + c;
-        if (v < V && k < d) Wt[(int64_t)v * d + k] = tile[c][r];
+    for (int i = threadIdx.x; i < 4 * 512; i += 256) {
+        const int q = i >> 9, l = (i >> 3) & 63, e = i & 7;    // k-tile in block, lane, element
+        const int kt = blockIdx.y * 4 + q;
+        if (kt < KT) P[tile_off(vt, kt, KT) + l * 8 + e] = tile[q * 16 + 8 * (l >> 5) + e][l & 31];
     }
 }
 
@@ -77,10 +113,11 @@ constexpr int KS = BK / 16;            // MFMA k-steps per block
 constexpr int A_LD = BK + 8;           // padded LDS row stride, bf16
 constexpr int A_PIECES = MB * BK / 8;  // 16-byte pieces per block
 constexpr int A_PER_T = A_PIECES / NT; // per thread (6)
-constexpr int WPF = 2 * KS;            // Wt prefetch depth in k-steps (two blocks)
+constexpr int RB = 2;                  // weight ring depth in LDS blocks
+constexpr int WPF = RB * KS;           // weight prefetch depth in k-steps
 static_assert(A_PIECES % NT == 0, "block pieces must split evenly");
 
-__global__ __launch_bounds__(NT, 1) void k_lmhead(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wt,
+__global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wp,
                                                   float* __restrict__ out, int M, int d, int V)
 {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][MB * A_LD];
@@ -88,21 +125,23 @@ __global__ __launch_bounds__(NT, 1) void k_lmhead(const uint16_t* __restrict__ H
     const int li = lane & 31, kg = lane >> 5;
     const int n0 = blockIdx.x * BN + wave * WN;
     const int m0 = blockIdx.y * MB;
-    const int nsteps = (d + 15) / 16;
+    const int nsteps = (d + 15) / 16;          // k-tiles per vocabulary tile
+    const int nvt = (V + 31) / 32;
     const int nblk = (d + BK - 1) / BK;
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    const bf16x8 zero = {};
 
-    // rows past V read the last valid row; their results are not stored
-    const uint16_t* bp[2];
+    // this lane's fragment of each k-tile of its vocabulary tile; tiles past
+    // the last read the last one (their results are not stored)
+    const uint16_t* bp[NC];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int v = min(n0 + 32 * c + li, V - 1);
-        bp[c] = Wt + (int64_t)v * d + 8 * kg;
+    for (int c = 0; c < NC; ++c) {
+        const int vt = min((n0 + 32 * c) / 32, nvt - 1);
+        bp[c] = Wp + tile_off(vt, 0, nsteps) + lane * 8;
     }
-    auto ldw = [&](int c, int step) -> bf16x8 {
-        return (step < nsteps && step * 16 + 8 * kg < d) ? ld16(bp[c] + step * 16) : zero;
-    };
+    // every load is issued, from an in-range address (a fixed count of loads
+    // per step lets the compiler wait for exactly the ones a use needs); a
+    // fragment past the last k-tile is never multiplied, so no select on the
+    // loaded value (one would make the block's end wait for the whole ring)
+    auto ldw = [&](int c, int step) -> bf16x8 { return ld16(bp[c] + (int64_t)(step < nsteps ? step : 0) * (TG * 512)); };
     // this thread's share of a hidden-state block: pieces tid + i*NT, i < 6,
     // held in six named registers (an indexable array would be moved to LDS)
     static_assert(A_PER_T == 6, "staging below is written out for six pieces");
@@ -115,73 +154,82 @@ __global__ __launch_bounds__(NT, 1) void k_lmhead(const uint16_t* __restrict__ H
     const uint16_t* hs4 = LM_SRC(4);
     const uint16_t* hs5 = LM_SRC(5);
 #undef LM_SRC
+    // columns past d are stored as zero (the weight's are zero there too,
+    // and a finite 0 * 0 keeps a non-finite hidden value elsewhere out); the
+    // select sits at the store, which waits for the loads anyway
     uint4 s0, s1, s2, s3, s4, s5;
+    uint32_t amask;                     // all ones while the loaded columns are below d
 #define LM_LOAD_A(kb)                                                                          \
     do {                                                                                       \
         const bool ok_ = (kb) < nblk && (kb) * BK + ac < d;                                   \
-        const int64_t o_ = (int64_t)(kb) * BK;                                                \
-        s0 = ok_ ? *reinterpret_cast<const uint4*>(hs0 + o_) : z4;                             \
-        s1 = ok_ ? *reinterpret_cast<const uint4*>(hs1 + o_) : z4;                             \
-        s2 = ok_ ? *reinterpret_cast<const uint4*>(hs2 + o_) : z4;                             \
-        s3 = ok_ ? *reinterpret_cast<const uint4*>(hs3 + o_) : z4;                             \
-        s4 = ok_ ? *reinterpret_cast<const uint4*>(hs4 + o_) : z4;                             \
-        s5 = ok_ ? *reinterpret_cast<const uint4*>(hs5 + o_) : z4;                             \
+        amask = ok_ ? ~0u : 0u;                                                               \
+        const int64_t o_ = ok_ ? (int64_t)(kb) * BK : 0;                                      \
+        s0 = *reinterpret_cast<const uint4*>(hs0 + o_);                                       \
+        s1 = *reinterpret_cast<const uint4*>(hs1 + o_);                                       \
+        s2 = *reinterpret_cast<const uint4*>(hs2 + o_);                                       \
+        s3 = *reinterpret_cast<const uint4*>(hs3 + o_);                                       \
+        s4 = *reinterpret_cast<const uint4*>(hs4 + o_);                                       \
+        s5 = *reinterpret_cast<const uint4*>(hs5 + o_);                                       \
     } while (0)
 #define LM_STORE_A(buf)                                                                        \
     do {                                                                                       \
         uint16_t* a_ = &As[buf][ar * A_LD + ac];                                              \
-        *reinterpret_cast<uint4*>(a_ + 0 * 32 * A_LD) = s0;                                   \
-        *reinterpret_cast<uint4*>(a_ + 1 * 32 * A_LD) = s1;                                   \
-        *reinterpret_cast<uint4*>(a_ + 2 * 32 * A_LD) = s2;                                   \
-        *reinterpret_cast<uint4*>(a_ + 3 * 32 * A_LD) = s3;                                   \
-        *reinterpret_cast<uint4*>(a_ + 4 * 32 * A_LD) = s4;                                   \
-        *reinterpret_cast<uint4*>(a_ + 5 * 32 * A_LD) = s5;                                   \
+        *reinterpret_cast<uint4*>(a_ + 0 * 32 * A_LD) = and4(s0, amask);                      \
+        *reinterpret_cast<uint4*>(a_ + 1 * 32 * A_LD) = and4(s1, amask);                      \
+        *reinterpret_cast<uint4*>(a_ + 2 * 32 * A_LD) = and4(s2, amask);                      \
+        *reinterpret_cast<uint4*>(a_ + 3 * 32 * A_LD) = and4(s3, amask);                      \
+        *reinterpret_cast<uint4*>(a_ + 4 * 32 * A_LD) = and4(s4, amask);                      \
+        *reinterpret_cast<uint4*>(a_ + 5 * 32 * A_LD) = and4(s5, amask);                      \
     } while (0)
 
-    f32x16 acc[MT][2];
+    f32x16 acc[MT][NC];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        acc[t][0] = f32x16{};
-        acc[t][1] = f32x16{};
-    }
-    bf16x8 wb[WPF][2];
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int q = 0; q < WPF; ++q) {
-        wb[q][0] = ldw(0, q);
-        wb[q][1] = ldw(1, q);
-    }
+        for (int c = 0; c < NC; ++c) acc[t][c] = f32x16{};
+    bf16x8 wb[WPF][NC];
+#pragma unroll
+    for (int q = 0; q < WPF; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) wb[q][c] = ldw(c, q);
     LM_LOAD_A(0);
     LM_STORE_A(0);
     LM_LOAD_A(1);
     __syncthreads();
 
-    // blocks in pairs so every Wt ring slot index is a compile-time constant
-    for (int kb0 = 0; kb0 < nblk; kb0 += 2) {
+    // blocks in groups of RB so every weight ring slot index is a compile-time
+    // constant; the hidden-state block alternates between the two LDS buffers
+    for (int kb0 = 0; kb0 < nblk; kb0 += RB) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < RB; ++h) {
             const int kb = kb0 + h;
             if (kb < nblk) {
-                const uint16_t* as = As[h] + li * A_LD + 8 * kg;
+                const int buf = kb & 1;
+                const uint16_t* as = As[buf] + li * A_LD + 8 * kg;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int step = kb * KS + ks;
                     const int slot = h * KS + ks;
-                    const bf16x8 b0 = wb[slot][0], b1 = wb[slot][1];
-                    wb[slot][0] = ldw(0, step + WPF);
-                    wb[slot][1] = ldw(1, step + WPF);
+                    bf16x8 bc[NC];
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        bc[c] = wb[slot][c];
+                        wb[slot][c] = ldw(c, step + WPF);
+                    }
                     if (step < nsteps) {
 #pragma unroll
                         for (int t = 0; t < MT; ++t) {
                             const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + t * 32 * A_LD + ks * 16);
-                            acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[t][0], 0, 0, 0);
-                            acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[t][1], 0, 0, 0);
+#pragma unroll
+                            for (int c = 0; c < NC; ++c)
+                                acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bc[c], acc[t][c], 0, 0, 0);
                         }
                     }
                 }
                 // block kb+1 (in registers) into the other buffer; every wave
                 // finished reading that buffer before the previous barrier
-                LM_STORE_A(h ^ 1);
-                __syncthreads();
+                LM_STORE_A(buf ^ 1);
+                lds_barrier();
                 LM_LOAD_A(kb + 2);
             }
         }
@@ -192,7 +240,7 @@ __global__ __launch_bounds__(NT, 1) void k_lmhead(const uint16_t* __restrict__ H
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NC; ++c) {
             const int col = n0 + 32 * c + li;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -205,12 +253,12 @@ __global__ __launch_bounds__(NT, 1) void k_lmhead(const uint16_t* __restrict__ H
 
 static bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-static int check_gemm(const void* hidden, const void* w_vd, int32_t M, int32_t d, int32_t V, const float* logits)
+static int check_gemm(const void* hidden, const void* w_packed, int32_t M, int32_t d, int32_t V, const float* logits)
 {
     if (M < 0 || d < 8 || d % 8 != 0 || V < 1) return SV_EINVAL;
     if (M == 0) return SV_OK;
-    if (!hidden || !w_vd || !logits) return SV_EINVAL;
-    if (!aligned_to(hidden, 16) || !aligned_to(w_vd, 16) || !aligned_to(logits, 4)) return SV_EINVAL;
+    if (!hidden || !w_packed || !logits) return SV_EINVAL;
+    if (!aligned_to(hidden, 16) || !aligned_to(w_packed, 16) || !aligned_to(logits, 4)) return SV_EINVAL;
     if ((V + (int64_t)BN - 1) / BN > INT_MAX || (M + (int64_t)MB - 1) / MB > 65535) return SV_EINVAL;
     return 1;
 }
@@ -219,31 +267,38 @@ static int check_gemm(const void* hidden, const void* w_vd, int32_t M, int32_t d
 
 extern "C" {
 
-int sv_lmhead_pack(const void* w_dv, void* w_vd, int32_t d, int32_t V, void* stream)
+size_t sv_lmhead_packed_bytes(int32_t d, int32_t V)
 {
-    if (d < 1 || V < 1 || !w_dv || !w_vd) return SV_EINVAL;
-    if (!svlm::aligned_to(w_dv, 2) || !svlm::aligned_to(w_vd, 2)) return SV_EINVAL;
+    if (d < 1 || V < 1) return 0;
+    const size_t groups = ((size_t)V + 32 * svlm::TG - 1) / (32 * svlm::TG);
+    return groups * svlm::TG * (size_t)((d + 15) / 16) * 512 * sizeof(uint16_t);
+}
+
+int sv_lmhead_pack(const void* w_dv, void* w_packed, int32_t d, int32_t V, void* stream)
+{
+    if (d < 1 || V < 1 || !w_dv || !w_packed) return SV_EINVAL;
+    if (!svlm::aligned_to(w_dv, 2) || !svlm::aligned_to(w_packed, 16)) return SV_EINVAL;
     if ((d + 63) / 64 > 65535) return SV_EINVAL;
-    const dim3 grid((unsigned)((V + 63) / 64), (unsigned)((d + 63) / 64));
+    const dim3 grid((unsigned)((V + 31) / 32), (unsigned)((d + 63) / 64));
     sv_launch_begin();
     hipLaunchKernelGGL(svlm::k_pack, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint16_t*>(w_dv), static_cast<uint16_t*>(w_vd), d, V);
+                       static_cast<const uint16_t*>(w_dv), static_cast<uint16_t*>(w_packed), d, V, (d + 15) / 16);
     return sv_launch_status();
 }
 
-int sv_lmhead(const void* hidden, const void* w_vd, int32_t M, int32_t d, int32_t V, float* logits,
+int sv_lmhead(const void* hidden, const void* w_packed, int32_t M, int32_t d, int32_t V, float* logits,
               void* stream)
 {
-    const int rc = svlm::check_gemm(hidden, w_vd, M, d, V, logits);
+    const int rc = svlm::check_gemm(hidden, w_packed, M, d, V, logits);
     if (rc <= 0) return rc;
     const dim3 grid((unsigned)((V + svlm::BN - 1) / svlm::BN), (unsigned)((M + svlm::MB - 1) / svlm::MB));
     sv_launch_begin();
     hipLaunchKernelGGL(svlm::k_lmhead, grid, dim3(svlm::NT), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_vd), logits, M, d, V);
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_packed), logits, M, d, V);
     return sv_launch_status();
 }
 
-int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* target_logits,
+int spec_lmhead_verify(const void* hidden, const void* w_packed, int32_t d, float* target_logits,
                        const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
                        const float* uniforms, float temperature, const uint8_t* greedy_flag,
                        int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
@@ -252,7 +307,7 @@ int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* t
     if (B < 0 || K < 0 || K > SV_MAX_K) return SV_EINVAL;
     if ((int64_t)B * (K + 1) > INT_MAX) return SV_EINVAL;
     const int32_t M = B * (K + 1);
-    int rc = svlm::check_gemm(hidden, w_vd, M, d, V, target_logits);
+    int rc = svlm::check_gemm(hidden, w_packed, M, d, V, target_logits);
     if (rc < 0) return rc;
     if (B == 0) return SV_OK;
     // every check of the verify step runs before anything is launched
@@ -260,7 +315,7 @@ int spec_lmhead_verify(const void* hidden, const void* w_vd, int32_t d, float* t
                          V, SV_F32, draft_dtype, accepted_len, out_tokens, diag, workspace, workspace_bytes,
                          stream, 1);
     if (rc != SV_OK) return rc;
-    rc = sv_lmhead(hidden, w_vd, M, d, V, target_logits, stream);
+    rc = sv_lmhead(hidden, w_packed, M, d, V, target_logits, stream);
     if (rc != SV_OK) return rc;
     return sv_verify_mixed(target_logits, draft_logits, draft_tokens, uniforms, temperature, greedy_flag, B, K,
                            V, SV_F32, draft_dtype, accepted_len, out_tokens, diag, workspace, workspace_bytes,

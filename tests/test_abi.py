@@ -126,6 +126,14 @@ def test_lmhead_pack_host_checks(lib):
     assert lib.sv_lmhead_pack(FAKE, FAKE, 0, 10, None) == binding.SV_EINVAL
     assert lib.sv_lmhead_pack(FAKE + 1, FAKE, 16, 10, None) == binding.SV_EINVAL
     assert lib.sv_lmhead_pack(None, FAKE, 16, 10, None) == binding.SV_EINVAL
+    assert lib.sv_lmhead_pack(FAKE, FAKE + 8, 16, 10, None) == binding.SV_EINVAL
+
+
+@pytest.mark.parametrize("d,V,want", [(0, 5, 0), (5, 0, 0), (1, 1, 8192), (16, 256, 8192), (17, 32, 16384),
+                                      (16, 257, 16384), (4096, 128256, 501 * 8 * 256 * 1024)])
+def test_lmhead_packed_bytes(lib, d, V, want):
+    # groups of eight 32-column x 16-k tiles of 1 KB
+    assert lib.sv_lmhead_packed_bytes(d, V) == want
 
 
 @pytest.mark.parametrize("kw", [dict(draft_dtype=5), dict(T=0.0), dict(K=64), dict(d=12),

@@ -40,15 +40,32 @@ def _rand_bf16(rng, shape, scale):
     return I.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale))
 
 
-@pytest.mark.parametrize("d,V", [(1, 1), (70, 333), (4096, 130)])
-def test_pack_is_a_transpose(dev, d, V):
+def _tiles(w):
+    """W [d, V] as the header's packed layout, built by numpy indexing: tile
+    (vt, kt) lane l element e = W[kt*16 + 8*(l//32) + e, vt*32 + l%32], the
+    tiles ordered (vt // 8, kt, vt % 8).  Returns the layout and a mask of the
+    elements the header defines (tiles past ceil(V/32) are not written)."""
+    d, V = w.shape
+    KT, G = -(-d // 16), -(-V // 256)
+    pad = np.zeros((KT * 16, G * 256), dtype=w.dtype)
+    pad[:d, :V] = w
+    g, kt, j, l, e = np.meshgrid(np.arange(G), np.arange(KT), np.arange(8), np.arange(64), np.arange(8),
+                                 indexing="ij")
+    vt = g * 8 + j
+    return pad[kt * 16 + 8 * (l // 32) + e, vt * 32 + l % 32].reshape(-1), (vt < -(-V // 32)).reshape(-1)
+
+
+@pytest.mark.parametrize("d,V", [(1, 1), (70, 333), (4096, 130), (72, 64)])
+def test_pack_layout(dev, d, V):
     import torch
     rng = np.random.default_rng(d + V)
     w = _rand_bf16(rng, (d, V), 1.0)
-    wt = binding.lmhead_pack(binding.bf16_tensor(w, dev))
+    pk = binding.lmhead_pack(binding.bf16_tensor(w, dev))
     torch.cuda.synchronize()
-    got = wt.view(torch.int16).cpu().numpy().view(np.uint16)
-    assert np.array_equal(got, w.T)
+    got = pk.data.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert got.size * 2 == binding.packed_bytes(d, V)
+    want, defined = _tiles(w)
+    assert np.array_equal(got[defined], want[defined])
 
 
 @pytest.mark.parametrize("M,d,V", [(1, 8, 1), (5, 24, 33), (192, 256, 1000), (200, 4096, 515),
@@ -75,9 +92,10 @@ def test_gemm_against_fp64_product(dev, M, d, V):
 def test_gemm_rejects_bad_shapes(dev):
     import torch
     h = torch.zeros(4, 12, dtype=torch.bfloat16, device=dev)
-    wt = torch.zeros(8, 12, dtype=torch.bfloat16, device=dev)
+    pk = binding.PackedWeight(torch.zeros(binding.packed_bytes(12, 8) // 2, dtype=torch.bfloat16, device=dev),
+                              12, 8)
     with pytest.raises(binding.SpecVerifyError):
-        binding.lmhead(h, wt)          # d = 12 is not a multiple of 8
+        binding.lmhead(h, pk)          # d = 12 is not a multiple of 8
 
 
 @pytest.mark.parametrize("mode,groups", [(binding.MODE_AUTO, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1)],
