@@ -79,6 +79,43 @@ def _timed(torch, stream, K, first, second):
     return (t1 - t0) * 1e3 / K, a, b
 
 
+FLUSH_NOTE = ("1 GiB read on the launch stream before every step (outside the events): the 256 MB "
+              "last-level cache then holds none of the inputs and no dirty lines")
+
+
+def _timed_cold(torch, stream, K, first, second, flush_mib=1024):
+    """K steps of first() then second(), each after reading flush_mib MiB on the
+    same stream so the 256 MB last-level cache holds none of the inputs (a read,
+    not a write: written lines would be written back during the timed part);
+    HIP events around each part (the flush is outside them)."""
+    import numpy as np
+    junk = torch.ones(flush_mib << 18, dtype=torch.float32, device=stream.device)
+    sink = torch.empty((), dtype=torch.float32, device=stream.device)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        torch.sum(junk, dim=0, out=sink)
+        evs[i][0].record(stream)
+        first()
+        evs[i][1].record(stream)
+        second()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    del junk
+    a = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
+    b = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
+    return a, b
+
+
+def _cold_report(np, dom, rest, nbytes):
+    """Cold-cache figures: medians of the dominant part and the rest, and the
+    dominant part's rate on its algorithmic bytes nbytes."""
+    return {"dominant_median_ms": float(np.median(dom)), "rest_median_ms": float(np.median(rest)),
+            "dominant_mean_ms": float(dom.mean()), "achieved": nbytes / (float(dom.mean()) * 1e-3) / 1e9,
+            "frac": nbytes / (float(dom.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "flush": FLUSH_NOTE}
+
+
 def _base_result(w, K, warmup, ms_per_step, dtype_name):
     return {
         "metric": METRIC,
@@ -136,6 +173,8 @@ def bench_verify(args, torch, np, binding, I, dev):
         call.draw()
     ms, stats_ms, draw_ms = _timed(torch, stream, args.steps, call.stats, call.draw)
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    cold_a, cold_b = _timed_cold(torch, stream, args.steps, call.stats, call.draw)
+    print(f"[bench] timed {args.steps} cold-cache steps", file=sys.stderr, flush=True)
 
     eager = I.eager_bytes(w)
     acc = out["accepted_len"].cpu().numpy()
@@ -164,7 +203,8 @@ def bench_verify(args, torch, np, binding, I, dev):
                                   binding.MODE_LAZY: "k_rowstats_lazy (all K+1 launches of a step)",
                                   binding.MODE_SEQ: "k_seq/k_seqg (the whole step, draw included)"}[sched],
                        "algorithmic_bytes_per_launch": stats_bytes,
-                       "avg_launch_ms": float(stats_ms.mean())}
+                       "avg_launch_ms": float(stats_ms.mean()),
+                       "cold": _cold_report(np, cold_a, cold_b, stats_bytes)}
     res["timing_ms"] = {"step_events_median": float(np.median(step_ev)),
                         "step_events_p10": float(np.percentile(step_ev, 10)),
                         "step_events_p90": float(np.percentile(step_ev, 90)),
@@ -277,6 +317,8 @@ def bench_lookup(args, torch, np, binding, I, dev):
         call.verify()
     ms, prop_ms, ver_ms = _timed(torch, stream, args.steps, call.propose, call.verify)
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    cold_p, cold_v = _timed_cold(torch, stream, args.steps, call.propose, call.verify)
+    print(f"[bench] timed {args.steps} cold-cache steps", file=sys.stderr, flush=True)
     klen = call.klen.cpu().numpy()
     out = call.outputs
     acc = out["accepted_len"].cpu().numpy()
@@ -302,7 +344,8 @@ def bench_lookup(args, torch, np, binding, I, dev):
                        "kernel": "spec_verify_lookup (one launch: k_seqg with one-hot proposals)",
                        "algorithmic_bytes_per_launch": ver_bytes, "avg_launch_ms": float(ver_ms.mean()),
                        "proposer_avg_ms": float(prop_ms.mean()), "proposer_history_bytes": hist_bytes,
-                       "proposer_gbs": hist_bytes / (float(prop_ms.mean()) * 1e-3) / 1e9}
+                       "proposer_gbs": hist_bytes / (float(prop_ms.mean()) * 1e-3) / 1e9,
+                       "cold": _cold_report(np, cold_v, cold_p, ver_bytes)}
     res["timing_ms"] = {"propose_median": float(np.median(prop_ms)), "verify_median": float(np.median(ver_ms)),
                         "step_events_median": float(np.median(prop_ms + ver_ms))}
     res["method"] = _method_stats(w, acc)
