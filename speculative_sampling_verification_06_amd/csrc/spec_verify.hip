@@ -1306,7 +1306,7 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
 constexpr int GT = 256;               // threads per workgroup
 constexpr int GW = GT / 64;
 constexpr int GU = 3;                 // 16-byte loads in flight per lane and row
-constexpr int GSPW = 2;               // draw: segments per wave per step
+constexpr int GDV = 8;                // draw: 16-byte pieces in flight per lane
 constexpr int GMAXG = 64;             // members per sequence at most (one wave gathers them)
 constexpr int GMAXSEG = 2048;         // segment sums of one slice held in LDS
 constexpr int GCAP = 4096;            // workgroups per launch at most (workspace sizing)
@@ -1377,6 +1377,92 @@ __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t e
         if (__all(ready)) return true;
         if (it >= GSPIN) return false;
         __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// Draw pass of one member over its slice (segments sg0 .. sg0+nl-1) of row
+// n: per segment, the sum of the draw weights (seg_r: residual max(0, p-q),
+// or p for the bonus row, both scaled by Z_p) and of p (seg_p).  Full
+// segments of 16-byte aligned rows go DSEG per wave step with every load of
+// the step issued, unconditionally and from in-range addresses, before any is
+// used, kept as raw 16-byte pieces (half the registers of unpacked floats);
+// a partial last segment or unaligned rows go one segment per wave at a
+// time.  Per element the arithmetic and its order are the walk's.
+template <int DTT, int DTD, bool OH, bool BONUS>
+__device__ __forceinline__ void draw_sums(const char* trow, const char* drow, int V, int nseg, int sg0, int nl,
+                                          float s, float cp, float cq, float w, int32_t ox, bool fast_rows,
+                                          float* seg_r, float* seg_p)
+{
+    constexpr int VT = Fmt<DTT>::BYTES / 2;        // 16-byte pieces per eight elements
+    constexpr int VD = Fmt<DTD>::BYTES / 2;
+    constexpr bool LD = !BONUS && !OH;             // a draft row to load
+    constexpr int DSEG = GDV / (VT + VD);          // segments per wave step
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool partial = (V % SEG) != 0 && sg0 + nl == nseg && nl > 0;
+    const int nfast = fast_rows ? nl - (partial ? 1 : 0) : 0;
+    for (int l0 = wave * DSEG; l0 < nfast; l0 += GW * DSEG) {
+        uint4 rt[DSEG][VT], rd[DSEG][LD ? VD : 1];
+#pragma unroll
+        for (int k = 0; k < DSEG; ++k) {
+            const int64_t e = (int64_t)(sg0 + min(l0 + k, nfast - 1)) * SEG + (int64_t)lane * LE;
+            const uint4* pt = reinterpret_cast<const uint4*>(trow + e * Fmt<DTT>::BYTES);
+#pragma unroll
+            for (int v = 0; v < VT; ++v) rt[k][v] = pt[v];
+            if constexpr (LD) {
+                const uint4* pd = reinterpret_cast<const uint4*>(drow + e * Fmt<DTD>::BYTES);
+#pragma unroll
+                for (int v = 0; v < VD; ++v) rd[k][v] = pd[v];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < DSEG; ++k) {
+            float xl[LE], xd[LE];
+#pragma unroll
+            for (int v = 0; v < VT; ++v) unpack<DTT>(rt[k][v], xl + v * (LE / VT));
+            if constexpr (LD) {
+#pragma unroll
+                for (int v = 0; v < VD; ++v) unpack<DTD>(rd[k][v], xd + v * (LE / VD));
+            } else if constexpr (OH && !BONUS) {
+                onehot8((int64_t)(sg0 + l0 + k) * SEG + (int64_t)lane * LE, ox, xd);
+            }
+            float sr = 0.f, sp = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < LE; ++qq) {
+                const float ep2 = ex2(__builtin_fmaf(xl[qq], s, -cp));
+                sp += ep2;
+                if constexpr (BONUS) sr += ep2;
+                else sr += weight(xl[qq], xd[qq], s, cp, cq, w, 0);
+            }
+            sr = wave_sum(sr);
+            sp = wave_sum(sp);
+            if (lane == 0 && l0 + k < nfast) {
+                seg_r[l0 + k] = sr;
+                seg_p[l0 + k] = sp;
+            }
+        }
+    }
+    const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+    const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
+    for (int l = nfast + wave; l < nl; l += GW) {
+        const int64_t e = (int64_t)(sg0 + l) * SEG + (int64_t)lane * LE;
+        float xl[LE], xd[LE];
+        load8<DTT>(trow, e, V, t_al, xl);
+        if constexpr (LD) load8<DTD>(drow, e, V, d_al, xd);
+        else if constexpr (OH && !BONUS) onehot8(e, ox, xd);
+        float sr = 0.f, sp = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < LE; ++qq) {
+            const float ep2 = ex2(__builtin_fmaf(xl[qq], s, -cp));
+            sp += ep2;
+            if constexpr (BONUS) sr += ep2;
+            else sr += weight(xl[qq], xd[qq], s, cp, cq, w, 0);
+        }
+        sr = wave_sum(sr);
+        sp = wave_sum(sp);
+        if (lane == 0) {
+            seg_r[l] = sr;
+            seg_p[l] = sp;
+        }
     }
 }
 
@@ -1531,34 +1617,9 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const float w = bonus ? 0.f : dec.zp / dec.zq;
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
-    for (int l0 = wave * GSPW; l0 < nl; l0 += GW * GSPW) {
-        float xl[GSPW][LE], xd[GSPW][LE];
-#pragma unroll
-        for (int k = 0; k < GSPW; ++k) {
-            const int64_t e = (int64_t)(sg0 + l0 + k) * SEG + (int64_t)lane * LE;
-            load8<DTT>(trow, e, V, t_al, xl[k]);
-            if (!bonus) {
-                if constexpr (OH) onehot8(e, ox, xd[k]);
-                else load8<DTD>(drow, e, V, d_al, xd[k]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < GSPW; ++k) {
-            float sr = 0.f, sp = 0.f;
-#pragma unroll
-            for (int qq = 0; qq < LE; ++qq) {
-                const float ep2 = ex2(__builtin_fmaf(xl[k][qq], s, -cp));
-                sp += ep2;
-                sr += bonus ? ep2 : weight(xl[k][qq], xd[k][qq], s, cp, cq, w, 0);
-            }
-            sr = wave_sum(sr);
-            sp = wave_sum(sp);
-            if (lane == 0 && l0 + k < nl) {
-                seg_r[l0 + k] = sr;
-                seg_p[l0 + k] = sp;
-            }
-        }
-    }
+    const bool fast_rows = t_al && (bonus || OH || d_al);
+    if (bonus) draw_sums<DTT, DTD, OH, true>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
+    else draw_sums<DTT, DTD, OH, false>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
     __syncthreads();
     float tr = 0.f, tp = 0.f;                      // slice totals, in the scan order the search uses
     for (int base = 0; base < nl; base += GT) {
