@@ -295,6 +295,18 @@ int sv_schedule(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t d
 int sv_set_seq_groups(int groups);
 int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
 
+/* Every wait of the SV_MODE_SEQ exchange is bounded: after this many polls
+ * (about 50 ns each) it gives up and the sequence reports accepted_len -1
+ * instead of hanging, e.g. when other work keeps some of the call's
+ * workgroups from running at the same time.  The default (polls = 0) is
+ * 2^20; smaller values are for tests that force the give-up path.  A
+ * sampling sequence's accepted_len is written by the workgroup that draws,
+ * after the drawn token, so a valid length always stands next to a written
+ * token.  Words a give-up leaves in the workspace carry that call's tags and
+ * never match a later call, except a replay of the same captured launch.
+ * Process-wide; SV_EINVAL for polls outside 0..2^20.                      */
+int sv_set_wait_limit(int32_t polls);
+
 /* The HIP error code (hipError_t) behind this thread's most recent
  * SV_ELAUNCH, 0 if none yet.  Entry points clear an error left by an earlier
  * HIP call of the caller before launching, so SV_ELAUNCH always means one of

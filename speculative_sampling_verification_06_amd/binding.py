@@ -23,7 +23,7 @@ SV_MAX_K = 63
 # The exported names, as declared in include/spec_verify.h.
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_packed_bytes", "sv_lmhead_pack", "sv_lmhead",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
-           "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups",
+           "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups", "sv_set_wait_limit",
            "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
            "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
@@ -109,6 +109,8 @@ def load_library(path: str = LIB_PATH):
             lib.sv_set_seq_groups.argtypes = [C.c_int]
             lib.sv_seq_groups.restype = C.c_int
             lib.sv_seq_groups.argtypes = [C.c_int32] * 5
+            lib.sv_set_wait_limit.restype = C.c_int
+            lib.sv_set_wait_limit.argtypes = [C.c_int32]
             lib.sv_lmhead_packed_bytes.restype = C.c_size_t
             lib.sv_lmhead_packed_bytes.argtypes = [C.c_int32, C.c_int32]
             lib.sv_lmhead_pack.restype = C.c_int
@@ -147,6 +149,13 @@ def get_mode() -> int:
 def set_seq_groups(groups: int) -> None:
     """Cap on workgroups per sequence under MODE_SEQ (0 = as many as the device holds)."""
     rc = load_library().sv_set_seq_groups(int(groups))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+
+
+def set_wait_limit(polls: int) -> None:
+    """Polls before a wait of the MODE_SEQ exchange gives up (0 = the default, 2**20)."""
+    rc = load_library().sv_set_wait_limit(int(polls))
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
 

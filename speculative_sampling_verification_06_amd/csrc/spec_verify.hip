@@ -113,6 +113,8 @@ struct Params {
     int32_t nseg, tiles;
     int32_t G, gsegs; // grouped schedule: workgroups per sequence, segments per workgroup slice
     uint32_t salt;    // grouped schedule: shape hash folded into the tags
+    uint32_t nonce;   // grouped schedule: per-call host counter folded into the tags
+    int32_t spin;     // grouped schedule: polls before a wait gives up
     const int32_t* klen;  // proposals per sequence (prompt lookup), null = K for all
     int32_t onehot;   // draft distribution = one-hot at the proposed token (no draft logits)
     float s;          // log2(e) / T
@@ -598,7 +600,7 @@ __device__ __forceinline__ TestIn load_test_in(const Params& P, int b, int j, bo
 // of the plain verify step.
 template <int DTT, int DTD, bool RAGGED = false>
 __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out, bool draw_here,
-                            const RowStat* f_rs, const TestIn* ti, Decision* dec)
+                            const RowStat* f_rs, const TestIn* ti, Decision* dec, bool acc_by_draw = false)
 {
     const int K = P.K;
     const float s = P.s;
@@ -677,7 +679,7 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
                 }
                 if (j <= K) put(P.lse_p, ub + j, seen ? (shift_of(f_rs[j].m, s) + log2f(f_rs[j].z)) * LN2 : NAN);
                 if (j == 0) {
-                    P.acc[b] = n;
+                    if (greedy || !acc_by_draw) P.acc[b] = n;
                     if (greedy) put(P.res_mass, b, 0.f);
                 }
             }
@@ -1350,7 +1352,7 @@ __device__ __forceinline__ int draw_word(int K, int G, int g, int w) { return (K
 // whether every member's words arrived (uniform over the wave).
 template <int NW>
 __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t ep, uint32_t salt, int first,
-                                       uint32_t (&v)[NW])
+                                       int spin, uint32_t (&v)[NW])
 {
     const int l = threadIdx.x & 63;
     bool ready = l >= G;
@@ -1375,7 +1377,7 @@ __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t e
             }
         }
         if (__all(ready)) return true;
-        if (it >= GSPIN) return false;
+        if (it >= spin) return false;
         __builtin_amdgcn_s_sleep(2);
     }
 }
@@ -1506,8 +1508,15 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     __shared__ int sh_pick_g, sh_pick_mode, sh_pick_over;
     __shared__ float sh_pick_S, sh_pick_thr;
 
-    uint32_t ep = 0;
-    if (wave == 0) ep = (uint32_t)__hip_atomic_load(P.gep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // call identity in the tags: the device counter (fresh for every replay of
+    // a captured launch) and the host's per-call nonce (so that words a
+    // member left in a call whose waits gave up never match a later call, even
+    // if that member read the counter after member 0 advanced it)
+    uint32_t ep0 = 0, ep = 0;
+    if (wave == 0) {
+        ep0 = (uint32_t)__hip_atomic_load(P.gep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ep = ep0 ^ mix32(P.nonce + 0x7f4a7c15u);
+    }
     if (tid < R) f_rs[tid] = tid > K ? d0 : RowStat{0.f, 0.f, 0, 0};
     const int tw = (GW - 1) * 64;                  // last wave loads the test inputs
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
@@ -1562,13 +1571,13 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
             const int first = pos_word(K, G, j, lane, 0);
             if (greedy) {
                 uint32_t v[2];
-                ok = gather<2>(region, G, ep, salt, first, v);
+                ok = gather<2>(region, G, ep, salt, first, P.spin, v);
                 AmState am = {NEG_INF, INT_MAX, 0u};
                 if (lane < G) am = {__uint_as_float(v[0]), (int32_t)(v[1] & 0x7fffffffu), v[1] >> 31};
                 t = rowstat_am(wave_reduce_am(am));
             } else if (dj) {
                 uint32_t v[4];
-                ok = gather<4>(region, G, ep, salt, first, v);
+                ok = gather<4>(region, G, ep, salt, first, P.spin, v);
                 SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
                 if (lane < G) {
                     st = {__uint_as_float(v[0]), __uint_as_float(v[1])};
@@ -1578,14 +1587,14 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                 d = rowstat_sm(wave_reduce_sm(sd, s));
             } else {
                 uint32_t v[2];
-                ok = gather<2>(region, G, ep, salt, first, v);
+                ok = gather<2>(region, G, ep, salt, first, P.spin, v);
                 SmState st = {NEG_INF, 0.f};
                 if (lane < G) st = {__uint_as_float(v[0]), __uint_as_float(v[1])};
                 t = rowstat_sm(wave_reduce_sm(st, s));
             }
             // every member has read the counter once position 0 is in
             if (j == 0 && g == 0 && lane == 0)
-                __hip_atomic_store(P.gep + b, ep + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(P.gep + b, ep0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (lane == 0) {
                 f_rs[j] = t;
                 if (dj) f_rs[K + 1 + j] = d;
@@ -1603,7 +1612,10 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         return;
     }
 
-    decide_core<DTT, DTD, OH>(P, b, greedy, g == 0, true, f_rs, ti, &dec);
+    // a valid sampling sequence's accepted length is written by the member
+    // that draws, after the drawn token: a member whose wait gave up writes
+    // -1, and a length can then only stand next to a token that was written
+    decide_core<DTT, DTD, OH>(P, b, greedy, g == 0, true, f_rs, ti, &dec, true);
     if (greedy || !dec.ok) return;                 // uniform across the workgroup
 
     // draw from row n: this member's slice of segment sums, then the totals
@@ -1636,7 +1648,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
             put_word(region + wi + 1, word_tag(ep, salt, wi + 1), __float_as_uint(tp));
         }
         uint32_t v[2];
-        const bool ok = gather<2>(region, G, ep, salt, draw_word(K, G, lane, 0), v);
+        const bool ok = gather<2>(region, G, ep, salt, draw_word(K, G, lane, 0), P.spin, v);
         const float mr = lane < G ? __uint_as_float(v[0]) : 0.f;
         const float mp = lane < G ? __uint_as_float(v[1]) : 0.f;
         // every lane walks the member totals in member order (same bits on all)
@@ -1698,6 +1710,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         if (lane == 0) {
             P.out[(int64_t)b * (K + 1) + n] = y;
             put(P.res_mass, b, pk.g < 0 ? NAN : (pk.mode == 2 ? 0.f : pk.S / dec.zp));
+            P.acc[b] = n;
         }
     }
 }
@@ -1720,6 +1733,10 @@ static std::atomic<int> g_mode{-1};
 // most workgroups per sequence under SV_MODE_SEQ, 0 = as many as fit
 // (sv_set_seq_groups; SV_SEQ_GROUPS in the environment)
 static std::atomic<int> g_groups{-1};
+// polls before a wait of the grouped schedule gives up (sv_set_wait_limit)
+static std::atomic<int> g_spin{GSPIN};
+// per-call nonce of the grouped schedule's tags
+static std::atomic<uint32_t> g_nonce{0};
 
 static int groups_now()
 {
@@ -1936,6 +1953,8 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->G = 1;
     P->gsegs = pl->nseg;
     P->salt = 0;
+    P->nonce = 0;
+    P->spin = GSPIN;
     P->klen = nullptr;
     P->onehot = onehot ? 1 : 0;
     if (pl->sched == SEQ) {
@@ -1957,6 +1976,8 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
             P->G = pl->G;
             P->gsegs = pl->gsegs;
             P->salt = h;
+            P->nonce = g_nonce.fetch_add(1u, std::memory_order_relaxed);
+            P->spin = g_spin.load(std::memory_order_relaxed);
         }
     }
     return 1;   // ready to launch
@@ -2173,6 +2194,13 @@ int sv_set_seq_groups(int groups)
 {
     if (groups < 0 || groups > sv::GMAXG) return SV_EINVAL;
     sv::g_groups.store(groups, std::memory_order_relaxed);
+    return SV_OK;
+}
+
+int sv_set_wait_limit(int32_t polls)
+{
+    if (polls < 0 || polls > sv::GSPIN) return SV_EINVAL;
+    sv::g_spin.store(polls == 0 ? sv::GSPIN : polls, std::memory_order_relaxed);
     return SV_OK;
 }
 

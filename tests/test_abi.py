@@ -149,6 +149,13 @@ def test_fused_verify_checks_everything_before_launch(lib, kw):
     assert rc in (binding.SV_EINVAL, binding.SV_EWORKSPACE)
 
 
+def test_wait_limit_knob(lib):
+    assert lib.sv_set_wait_limit(-1) == binding.SV_EINVAL
+    assert lib.sv_set_wait_limit((1 << 20) + 1) == binding.SV_EINVAL
+    for polls in (1, 1 << 20, 0):                  # 0 restores the default
+        assert lib.sv_set_wait_limit(polls) == binding.SV_OK
+
+
 def test_mode_knob(lib):
     assert lib.sv_set_mode(4) == binding.SV_EINVAL and lib.sv_set_mode(-1) == binding.SV_EINVAL
     old = lib.sv_get_mode()

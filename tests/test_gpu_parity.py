@@ -297,6 +297,48 @@ def test_schedules_mixed_storage(dev, schedule, target_f32, V):
     check(I.Workload(w.name, w.B, w.K, w.V, dt, w.T, tgt, drf, w.tokens, w.uniforms, w.greedy), dev)
 
 
+def _subset(w, idx):
+    """The workload of the sequences idx only (same logits, tokens and uniforms)."""
+    dr = None if w.draft is None else w.draft[idx]
+    return I.Workload(w.name + "_sub", len(idx), w.K, w.V, w.dtype, w.T, w.target[idx], dr, w.tokens[idx],
+                      w.uniforms[idx], w.greedy[idx])
+
+
+def test_seq_wait_give_up_marks_invalid_then_recovers(dev):
+    """Every wait of the per-sequence exchange bounded to one poll from the host
+    (the kernels still run to the end): each sequence is either reported invalid
+    or agrees with the oracle, never a length without its drawn token; the next
+    call on the same workspace with the default bound agrees with the oracle
+    everywhere (no word the failed call left is taken for a fresh one)."""
+    import torch
+    mask = (np.arange(64) % 5 == 2).astype(np.uint8)
+    w = I.synth_logits(4242, 64, 6, 20000, dtype=I.BF16, T=0.9, sigma=3.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=0.4, greedy_mask=mask, name="giveup")
+    binding.set_mode(binding.MODE_SEQ)
+    binding.set_seq_groups(0)
+    try:
+        assert binding.seq_groups(w.B, w.K, w.V, w.dtype) >= 2
+        ws = torch.zeros(binding.workspace_bytes(w.B, w.K, w.V, w.dtype), dtype=torch.uint8, device=dev)
+        o = oracle.verify(w)
+        binding.set_wait_limit(1)
+        _log("[giveup] one poll per wait")
+        g = run_gpu(w, dev, workspace=ws)
+        bad = g["accepted_len"] == -1
+        _log(f"[giveup] {int(bad.sum())} of {w.B} sequences gave up")
+        assert bad.any()
+        ok = np.where(~bad)[0]
+        if len(ok):
+            ws_ = _subset(w, ok)
+            parity.compare(ws_, {k: v[ok] for k, v in g.items()}, oracle.verify(ws_))
+        binding.set_wait_limit(0)
+        for rep in range(2):
+            g2 = run_gpu(w, dev, workspace=ws)
+            _log(f"[giveup] default bound, call {rep}: {parity.compare(w, g2, o)}")
+    finally:
+        binding.set_wait_limit(0)
+        binding.set_mode(binding.MODE_AUTO)
+
+
 def test_lazy_reads_only_reached_rows(dev):
     """A NaN planted in a row after the first rejection is never read by the
     lazy and per-sequence schedules (the eager stream reads it but the method
