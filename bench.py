@@ -60,12 +60,20 @@ def _traffic(kernel: str, workload_name: str, source: str):
 
 
 def _timed(torch, stream, K, first, second):
-    """K steps of first() then second(), HIP events around each on the launch
-    stream; returns (host ms per step, first ms array, second ms array)."""
+    """K steps of first() then second() between two synchronizations, nothing
+    else in between (host ms per step); then K more with HIP events around each
+    part on the launch stream (an event record is a queue packet of its own, so
+    those steps are not the ones the host clock times).  Returns (host ms per
+    step, first ms array, second ms array)."""
     import numpy as np
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(K):
+        first()
+        second()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
         evs[i][0].record(stream)
         first()
@@ -73,7 +81,6 @@ def _timed(torch, stream, K, first, second):
         second()
         evs[i][2].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     a = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
     b = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
     return (t1 - t0) * 1e3 / K, a, b
@@ -261,16 +268,21 @@ def bench_lmhead(args, torch, np, binding, I, dev):
 
 
 def _timed_one(torch, stream, K, fn):
+    """As _timed for a one-part step: host ms per step over K bare steps, then
+    the event-timed ms of K more."""
     import numpy as np
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(K):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for i in range(K):
         evs[i][0].record(stream)
         fn()
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / K, np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
 
 
@@ -400,7 +412,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="cfg152k",
-                    choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead", "sample", "kvcommit", "lookup"])
+                    choices=["cfg152k", "cfg128k", "cfg32k", "tiny", "lmhead", "sample", "kvcommit", "lookup",
+                             "shard_batch", "shard_vocab"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the oracle timing (repeated whole-workload calls)")

@@ -188,7 +188,16 @@ def cfg_128k(seed: int = 1002, B: int = 64) -> Workload:
 def cfg_152k(seed: int = 1003, B: int = 256) -> Workload:
     """B=256, K=8, V=152064 bf16; l = N(0,4) + zipf; d = l + N(0,2.5); T=1, sampling."""
     return synth_logits(seed, B, 8, 152064, dtype=BF16, T=1.0, sigma=4.0, zipf=True,
-                        draft_scale=1.0, draft_sigma=2.5, name="B256_K8_V152064_bf16")
+                        draft_scale=1.0, draft_sigma=2.5, name=f"B{B}_K8_V152064_bf16")
+
+
+def cfg_vocab_shard(seed: int = 1003, B: int = 256, shards: int = 8) -> Workload:
+    """One GPU's share of the B=256, K=8, V=152064 workload when the LM head is
+    split over the vocabulary: the first V/shards = 19008 columns (the head of
+    the Zipf bias), same recipe otherwise."""
+    V = 152064 // shards
+    return synth_logits(seed, B, 8, V, dtype=BF16, T=1.0, sigma=4.0, zipf=True,
+                        draft_scale=1.0, draft_sigma=2.5, name=f"B{B}_K8_V{V}_bf16_vocab_shard")
 
 
 def cfg_lmhead(seed: int = 1004, B: int = 32, K: int = 5, d: int = 4096, V: int = 128256,
@@ -230,6 +239,9 @@ CONFIGS = {
     "cfg128k": cfg_128k,
     "cfg152k": cfg_152k,
     "lmhead": cfg_lmhead,
+    # one GPU's share of cfg152k over 8 GPUs: by batch, or by vocabulary
+    "shard_batch": lambda seed=1003: cfg_152k(seed, B=32),
+    "shard_vocab": cfg_vocab_shard,
 }
 
 

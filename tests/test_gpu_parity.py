@@ -251,8 +251,9 @@ SCHED = pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.M
 
 @SCHED
 @pytest.mark.parametrize("make", [lambda: I.tiny(), lambda: I.tiny(greedy=True), lambda: I.cfg_32k(),
-                                  lambda: I.cfg_128k(), lambda: I.cfg_152k()],
-                         ids=["tiny", "tiny_greedy", "32k", "128k", "152k"])
+                                  lambda: I.cfg_128k(), lambda: I.cfg_152k(), I.CONFIGS["shard_batch"],
+                                  I.CONFIGS["shard_vocab"]],
+                         ids=["tiny", "tiny_greedy", "32k", "128k", "152k", "shard_batch", "shard_vocab"])
 def test_schedules_named_workloads(dev, schedule, make):
     check(make(), dev)
 
