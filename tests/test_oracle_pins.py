@@ -419,3 +419,30 @@ def test_lmhead_product_exact_on_integers():
     assert np.array_equal(got, want)
     sub = oracle.lmhead_logits(hb, wb, rows=[2, 0])
     assert np.array_equal(sub, want[[2, 0]])
+
+
+def test_lmhead_product_within_fp64_bound_on_general_values():
+    """General bf16 values (the workload's N(0,1) hidden states and N(0,0.02)
+    weights): each oracle logit lies within the fp64 summation bound
+    d * 2^-53 * sum|h_k w_k| of the exact rational dot product (Fraction
+    arithmetic, independent of numpy), and far inside the gap a dropped term
+    or a wrong index would open."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    B, K1, d, V = 2, 3, 96, 7
+    hb = I.f32_to_bf16_bits(rng.standard_normal((B, K1, d)).astype(np.float32))
+    wb = I.f32_to_bf16_bits((rng.standard_normal((d, V)) * 0.02).astype(np.float32))
+    hv = I.bf16_bits_to_f32(hb).astype(np.float64)
+    wv = I.bf16_bits_to_f32(wb).astype(np.float64)
+    got = oracle.lmhead_logits(hb, wb)
+    u = 2.0 ** -53
+    for b in range(B):
+        for k in range(K1):
+            for v in range(V):
+                exact = sum(Fraction(hv[b, k, i]) * Fraction(wv[i, v]) for i in range(d))
+                mag = float(sum(abs(Fraction(hv[b, k, i]) * Fraction(wv[i, v])) for i in range(d)))
+                err = abs(Fraction(got[b, k, v]) - exact)
+                assert float(err) <= d * u * mag
+                # every nonzero term is larger than that bound: dropping one is caught
+                smallest = min(abs(hv[b, k, i] * wv[i, v]) for i in range(d) if hv[b, k, i] * wv[i, v] != 0)
+                assert d * u * mag < smallest
