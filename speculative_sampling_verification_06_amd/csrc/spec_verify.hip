@@ -1075,7 +1075,22 @@ constexpr int QMAXSEG = 4096;         // segment sums held in LDS: V <= QMAXSEG 
 // (may be null), both streamed in the same loop by BT threads with U 16-byte
 // loads in flight per lane and row.  e0 is a multiple of 8 elements; e1 is a
 // multiple of 8 or the row end.
-template <int DTT, int DTD, int BT, int U>
+// Fair share for a stream every wave of the chip runs at once: the SIMD issues
+// the oldest ready wave first, so the waves dispatched last would get the
+// least issue and memory bandwidth and finish last.  Each wave lowers its
+// priority as it gets through its share (3 at the start, 0 in its last
+// quarter): waves that are ahead yield to the ones behind, and all finish
+// together.  `it` and `n` are uniform over the wave.
+__device__ __forceinline__ void fair_priority(int it, int n)
+{
+    const int p = 3 - (4 * it) / (n > 0 ? n : 1);
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
+template <int DTT, int DTD, int BT, int U, bool FAIR = false>
 __device__ __forceinline__ void stream_pair(const char* trow, const char* drow, int64_t e0, int64_t e1, float s,
                                             SmState& st, SmState& sd)
 {
@@ -1090,7 +1105,10 @@ __device__ __forceinline__ void stream_pair(const char* trow, const char* drow, 
         const int64_t d0 = e0 / ED, d1 = drow ? e1 / ED : d0;
         const int64_t nt = t1 - t0, nd = d1 - d0;
         const int64_t nv = nt > nd ? nt : nd;
-        for (int64_t k = tid; k < nv; k += (int64_t)BT * U) {
+        const int niter = (int)((nv + (int64_t)BT * U - 1) / ((int64_t)BT * U));
+        int it = 0;
+        for (int64_t k = tid; k < nv; k += (int64_t)BT * U, ++it) {
+            if constexpr (FAIR) fair_priority(it, niter);
             uint4 rt[U], rd[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -1309,6 +1327,12 @@ constexpr int GT = 256;               // threads per workgroup
 constexpr int GW = GT / 64;
 constexpr int GU = 3;                 // 16-byte loads in flight per lane and row
 constexpr int GDV = 8;                // draw: 16-byte pieces in flight per lane
+// Wave priorities (s_setprio): position 0 of every sequence streams with a
+// fair share (3 falling to 0 with progress); a sequence past it is on its way
+// to a decision and maybe a long chain of positions, ahead of every stream of
+// position 0; its draw, the end of a sequence, behind the chains.
+constexpr int PRIO_CHAIN = 3;
+constexpr int PRIO_DRAW = 1;
 constexpr int GMAXG = 64;             // members per sequence at most (one wave gathers them)
 constexpr int GMAXSEG = 2048;         // segment sums of one slice held in LDS
 constexpr int GCAP = 4096;            // workgroups per launch at most (workspace sizing)
@@ -1530,11 +1554,19 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
             SmState sm = {NEG_INF, 0.f};
             AmState am = {NEG_INF, INT_MAX, 0u};
             if (e0 < e1) scan_chunk<DTT, true, GT, GU>(trow, e0, e1, s, sm, am);
+            if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
             am = wave_reduce_am(am);
             if (lane == 0) sh_a[wave] = am;
         } else {
             SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
-            if (e0 < e1) stream_pair<DTT, DTD, GT, GU>(trow, dj ? draft_row<DTD>(P, b, j) : nullptr, e0, e1, s, st, sd);
+            // position 0: every sequence streams at once (fair share); later
+            // positions: the few long sequences, oldest-first is fine
+            const char* drow = dj ? draft_row<DTD>(P, b, j) : nullptr;
+            if (e0 < e1) {
+                if (j == 0) stream_pair<DTT, DTD, GT, GU, true>(trow, drow, e0, e1, s, st, sd);
+                else stream_pair<DTT, DTD, GT, GU>(trow, drow, e0, e1, s, st, sd);
+            }
+            if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
             st = wave_reduce_sm(st, s);
             if (dj) sd = wave_reduce_sm(sd, s);
             if (lane == 0) {
@@ -1630,6 +1662,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
     const bool fast_rows = t_al && (bonus || OH || d_al);
+    __builtin_amdgcn_s_setprio(PRIO_DRAW);
     if (bonus) draw_sums<DTT, DTD, OH, true>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
     else draw_sums<DTT, DTD, OH, false>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
     __syncthreads();
