@@ -296,9 +296,14 @@ int sv_set_seq_groups(int groups);
 int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
 
 /* Every wait of the SV_MODE_SEQ exchange is bounded: after this many polls
- * (about 50 ns each) it gives up and the sequence reports accepted_len -1
+ * (each one load round trip, about 0.5-1 us, so the default bounds a wait
+ * at roughly a second) it gives up and the sequence reports accepted_len -1
  * instead of hanging, e.g. when other work keeps some of the call's
- * workgroups from running at the same time.  The default (polls = 0) is
+ * workgroups from running at the same time: a launch of this schedule
+ * assumes the device holds all its workgroups at once, so verify calls in
+ * flight together on several streams (or next to other work that fills the
+ * device) belong under SV_MODE_EAGER or SV_MODE_LAZY, or in one stream's
+ * order.  The default (polls = 0) is
  * 2^20; smaller values are for tests that force the give-up path.  A
  * sampling sequence's accepted_len is written by the workgroup that draws,
  * after the drawn token, so a valid length always stands next to a written

@@ -3,7 +3,7 @@
 Every step of the verify path runs in the HIP kernels behind the C ABI in
 include/spec_verify.h.  torch supplies device memory and the stream; this
 module only checks shapes and dtypes, passes data pointers and the current
-stream, and keeps one zero-initialised workspace per device.  There is no
+stream, and keeps one zero-initialised workspace per device and stream.  There is no
 CPU fallback: if the library is missing or no GPU is present, calls raise.
 """
 
@@ -187,13 +187,15 @@ def _torch():
 _ws_cache: dict = {}
 
 
-def get_workspace(nbytes: int, device):
-    """A workspace of at least nbytes on `device`, reused across calls.
-
-    Calls that share it are ordered on the caller's stream.
-    """
+def get_workspace(nbytes: int, device, stream=None):
+    """A zero-initialised workspace of at least nbytes on `device`, reused by
+    the calls on one stream (raw HIP stream handle; None = the current one):
+    calls sharing a workspace must be ordered, and calls on different streams
+    may overlap, so each stream gets its own."""
     torch = _torch()
-    key = (str(device),)
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    key = (str(device), int(stream or 0))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -266,9 +268,9 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
     if "p_tok" in outputs:
         dg = SvDiag(*[_dev_ptr(outputs[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
     need = lib.sv_workspace_bytes(B, K, V, dt)
-    ws = workspace if workspace is not None else get_workspace(need, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = workspace if workspace is not None else get_workspace(need, dev, stream)
     dts = (dt,) if ddt == dt else (dt, ddt)
     if ddt != dt:
         fn_name = "spec_verify_ex"
@@ -347,9 +349,9 @@ class Bound:
         self._dg = None
         if "p_tok" in o:
             self._dg = SvDiag(*[_dev_ptr(o[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
-        ws = get_workspace(lib.sv_workspace_bytes(B, K, V, dt), target.device)
         if stream is None:
             stream = torch.cuda.current_stream(target.device).cuda_stream
+        ws = get_workspace(lib.sv_workspace_bytes(B, K, V, dt), target.device, stream)
         self._keep = (target, draft, tokens, uniforms, greedy, ws)
         self._args = (
             C.c_void_p(target.data_ptr()), C.c_void_p(None if draft is None else draft.data_ptr()),
@@ -495,9 +497,9 @@ def lmhead_verify(hidden, packed, draft, tokens, uniforms, temperature, greedy=N
                  lse_p=torch.empty(B, K + 1, device=dev), lse_q=torch.empty(B, K, device=dev),
                  res_mass=torch.empty(B, device=dev))
         dg = SvDiag(*[o[k].data_ptr() for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
-    ws = get_workspace(lib.sv_workspace_bytes(B, K, V, SV_F32), dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = get_workspace(lib.sv_workspace_bytes(B, K, V, SV_F32), dev, stream)
     ddt = SV_F32 if draft is None else _dtype_code(draft)
     _check_rc(lib.spec_lmhead_verify(
         hidden.data_ptr(), packed.data.data_ptr(), d, target_logits.data_ptr(),
@@ -537,9 +539,9 @@ def sample(logits, uniforms, temperature, greedy=None, *, lse=False, stream=None
     tokens = torch.empty(B, dtype=torch.int32, device=dev)
     out_lse = torch.empty(B, dtype=torch.float32, device=dev) if lse else None
     need = lib.sv_sample_workspace_bytes(B, V, dt)
-    ws = get_workspace(need, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = get_workspace(need, dev, stream)
     _check_rc(lib.sv_sample(logits.data_ptr() if B else None, dt, uniforms.data_ptr() if B else None,
                             C.c_float(float(temperature)), None if greedy is None else greedy.data_ptr(), B, V,
                             tokens.data_ptr() if B else None, None if out_lse is None else out_lse.data_ptr(),
@@ -600,9 +602,9 @@ def verify_lookup(target, cand, klen, uniforms, temperature, greedy=None, *, dia
                        res_mass=torch.empty(B, dtype=torch.float32, device=dev))
         dg = SvDiag(*[_dev_ptr(outputs[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
     need = lib.sv_workspace_bytes(B, K, V, dt)
-    ws = workspace if workspace is not None else get_workspace(need, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    ws = workspace if workspace is not None else get_workspace(need, dev, stream)
     _check_rc(lib.spec_verify_lookup(
         target.data_ptr() if B else None, dt, _dev_ptr(cand, "cand"), _dev_ptr(klen, "klen"),
         _dev_ptr(uniforms, "uniforms"), C.c_float(float(temperature)), _dev_ptr(greedy, "greedy_flag"), B, K, V,
@@ -631,9 +633,9 @@ class BoundLookup:
         self._dg = None
         if "p_tok" in o:
             self._dg = SvDiag(*[_dev_ptr(o[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
-        ws = get_workspace(lib.sv_workspace_bytes(B, K, V, dt), target.device)
         if stream is None:
             stream = torch.cuda.current_stream(target.device).cuda_stream
+        ws = get_workspace(lib.sv_workspace_bytes(B, K, V, dt), target.device, stream)
         self._keep = (history, hist_len, target, uniforms, greedy, ws)
         Lmax = history.shape[1]
         self._pargs = (C.c_void_p(_dev_ptr(history, "history")), C.c_void_p(_dev_ptr(hist_len, "hist_len")),
@@ -715,9 +717,9 @@ class BoundSample:
         B, V = logits.shape
         dt = _dtype_code(logits)
         lib = load_library()
-        ws = get_workspace(lib.sv_sample_workspace_bytes(B, V, dt), logits.device)
         if stream is None:
             stream = torch.cuda.current_stream(logits.device).cuda_stream
+        ws = get_workspace(lib.sv_sample_workspace_bytes(B, V, dt), logits.device, stream)
         self._keep = (logits, uniforms, greedy, ws)
         self._fn = lib.sv_sample
         self._args = (C.c_void_p(logits.data_ptr()), C.c_int32(dt), C.c_void_p(uniforms.data_ptr()),

@@ -340,6 +340,33 @@ def test_seq_wait_give_up_marks_invalid_then_recovers(dev):
         binding.set_mode(binding.MODE_AUTO)
 
 
+def test_two_streams_at_once(dev):
+    """Two calls in flight on two streams (default priority) at the same time:
+    the binding gives each stream its own workspace, and both agree with the
+    oracle.  Eager schedule: its partials live in the workspace, and it makes
+    no assumption about which workgroups run at once (the per-sequence one
+    does, see sv_set_wait_limit)."""
+    import torch
+    ws_ = [I.synth_logits(900 + i, 48, 5, 30000, dtype=I.BF16, T=0.9, sigma=3.0, zipf=True, draft_scale=1.0,
+                          draft_sigma=0.3 + 0.5 * i, name=f"streams_{i}") for i in range(2)]
+    binding.set_mode(binding.MODE_EAGER)
+    try:
+        ds = [binding.to_device(w, dev) for w in ws_]
+        streams = [torch.cuda.Stream(device=dev) for _ in ws_]
+        torch.cuda.synchronize()
+        outs = []
+        for d, st in zip(ds, streams):
+            with torch.cuda.stream(st):
+                outs.append(binding.verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
+                                           d["greedy"]))
+        torch.cuda.synchronize()
+        for w, out in zip(ws_, outs):
+            g = {k: v.cpu().numpy() for k, v in out.items()}
+            _log(f"[streams] {w.name}: {parity.compare(w, g, oracle.verify(w))}")
+    finally:
+        binding.set_mode(binding.MODE_AUTO)
+
+
 def test_lazy_reads_only_reached_rows(dev):
     """A NaN planted in a row after the first rejection is never read by the
     lazy and per-sequence schedules (the eager stream reads it but the method
