@@ -10,14 +10,18 @@ sampling (target ~ N(0,4) + log-Zipf bias, draft = target + N(0,2.5)).
 [32, 6, 4096] x W bf16 [4096, 128256] -> fp32 target logits, then the verify
 step against bf16 draft logits; one step = GEMM + verify).
 
-Prints one JSON line: verified logits/s (B*(K+1)*V per second), the roofline of
-the dominant kernel (k_rowstats for the verify workloads: algorithmic bytes =
-every target row and every draft row of sampling sequences read once, V*s
-bytes per row; k_lmhead for the LM-head workload: the weight read once plus
-the hidden states and the fp32 logits, with its MFMA rate beside it), each
-divided by the kernel's average duration from HIP events recorded around it
-on the launch stream, and the fp64 oracle's throughput on this host as a CPU
-baseline.
+Prints one JSON line: verified logits/s (B*(K+1)*V per second, host clock over
+bare steps), the roofline of the dominant kernel and the fp64 oracle's
+throughput on this host as a CPU baseline.  The dominant kernel depends on the
+schedule the shape gets: under the per-sequence schedule (the default
+workload) the whole step is one launch (k_seqg / k_seq), whose algorithmic
+bytes are the rows the method reaches plus the draw's pass over row n; under
+the eager schedule k_rowstats, every target row and every draft row of
+sampling sequences read once (V*s bytes per row); under the lazy schedule the
+row-statistics launches over the rows reached; for the LM-head workload
+k_lmhead (the weight read once plus the hidden states and the fp32 logits,
+with its MFMA rate beside it).  Each is divided by the kernel's average
+duration from HIP events recorded around it on the launch stream.
 """
 
 from __future__ import annotations
@@ -150,7 +154,7 @@ def _method_stats(w, acc):
 
 SCHEDULES = {1: "eager (one launch streams every row)",
              2: "lazy (one launch per position, reached rows only)",
-             3: "seq (one workgroup per sequence walks its positions, reached rows only, draws in place)"}
+             3: "seq (one launch: each sequence's workgroups walk its positions, reached rows only, draws in place)"}
 
 
 def _copy_calibration(args, torch, dev):
