@@ -22,9 +22,11 @@
 // W element is read from HBM exactly once and each 16-k step issues 12
 // v_mfma_f32_32x32x16_bf16 on one A fragment per tile pair (the 192
 // accumulators sit in AGPRs).  Weight tiles stream into a register ring RB
-// 64-k blocks deep; the hidden states (1.5 MB, L2-resident) come through a
-// double-buffered LDS block shared by the four waves, the next block's loads
-// in flight while the current one is multiplied.
+// 64-k blocks deep, with non-temporal loads; the hidden states (1.5 MB,
+// L2-resident) come through a double-buffered LDS block shared by the four
+// waves, the next block's loads in flight while the current one is
+// multiplied, and each wave reads the A fragments of the next 16-k step from
+// LDS while the matrix cores work on the current one.
 // Accumulation is fp32; bf16 x bf16 products are exact in fp32.
 //
 // MFMA 32x32x16 operand layout (lane l, 8 bf16 per operand):
@@ -77,9 +79,13 @@ __device__ __forceinline__ void lds_barrier()
 
 __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 
+// Weight fragments are read once: non-temporal loads (evict first), so the
+// stream does not push the hidden states, and the logits the verify step
+// reads next, out of the caches.
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p)
 {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -142,44 +148,32 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
     // fragment past the last k-tile is never multiplied, so no select on the
     // loaded value (one would make the block's end wait for the whole ring)
     auto ldw = [&](int c, int step) -> bf16x8 { return ld16(bp[c] + (int64_t)(step < nsteps ? step : 0) * (TG * 512)); };
-    // this thread's share of a hidden-state block: pieces tid + i*NT, i < 6,
-    // held in six named registers (an indexable array would be moved to LDS)
-    static_assert(A_PER_T == 6, "staging below is written out for six pieces");
-    const int ar = tid >> 3, ac = (tid & 7) * 8;               // piece i: row ar + 32*i
-#define LM_SRC(i) (H + (int64_t)min(m0 + ar + 32 * (i), M - 1) * d + ac)
-    const uint16_t* hs0 = LM_SRC(0);
-    const uint16_t* hs1 = LM_SRC(1);
-    const uint16_t* hs2 = LM_SRC(2);
-    const uint16_t* hs3 = LM_SRC(3);
-    const uint16_t* hs4 = LM_SRC(4);
-    const uint16_t* hs5 = LM_SRC(5);
-#undef LM_SRC
+    // this thread's share of a hidden-state block: A_PER_T pieces, rows
+    // ar + RP*i, columns ac .. ac+7 of the block
+    constexpr int PPR = BK / 8;                                 // pieces per row
+    constexpr int RP = NT / PPR;                                // rows per pass
+    const int ar = tid / PPR, ac = (tid % PPR) * 8;
+    const uint16_t* hs[A_PER_T];
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) hs[i] = H + (int64_t)min(m0 + ar + RP * i, M - 1) * d + ac;
     // columns past d are stored as zero (the weight's are zero there too,
     // and a finite 0 * 0 keeps a non-finite hidden value elsewhere out); the
     // select sits at the store, which waits for the loads anyway
-    uint4 s0, s1, s2, s3, s4, s5;
+    uint4 sa[A_PER_T];
     uint32_t amask;                     // all ones while the loaded columns are below d
 #define LM_LOAD_A(kb)                                                                          \
     do {                                                                                       \
         const bool ok_ = (kb) < nblk && (kb) * BK + ac < d;                                   \
         amask = ok_ ? ~0u : 0u;                                                               \
         const int64_t o_ = ok_ ? (int64_t)(kb) * BK : 0;                                      \
-        s0 = *reinterpret_cast<const uint4*>(hs0 + o_);                                       \
-        s1 = *reinterpret_cast<const uint4*>(hs1 + o_);                                       \
-        s2 = *reinterpret_cast<const uint4*>(hs2 + o_);                                       \
-        s3 = *reinterpret_cast<const uint4*>(hs3 + o_);                                       \
-        s4 = *reinterpret_cast<const uint4*>(hs4 + o_);                                       \
-        s5 = *reinterpret_cast<const uint4*>(hs5 + o_);                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < A_PER_T; ++i_)                               \
+            sa[i_] = *reinterpret_cast<const uint4*>(hs[i_] + o_);                            \
     } while (0)
 #define LM_STORE_A(buf)                                                                        \
     do {                                                                                       \
         uint16_t* a_ = &As[buf][ar * A_LD + ac];                                              \
-        *reinterpret_cast<uint4*>(a_ + 0 * 32 * A_LD) = and4(s0, amask);                      \
-        *reinterpret_cast<uint4*>(a_ + 1 * 32 * A_LD) = and4(s1, amask);                      \
-        *reinterpret_cast<uint4*>(a_ + 2 * 32 * A_LD) = and4(s2, amask);                      \
-        *reinterpret_cast<uint4*>(a_ + 3 * 32 * A_LD) = and4(s3, amask);                      \
-        *reinterpret_cast<uint4*>(a_ + 4 * 32 * A_LD) = and4(s4, amask);                      \
-        *reinterpret_cast<uint4*>(a_ + 5 * 32 * A_LD) = and4(s5, amask);                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < A_PER_T; ++i_)                               \
+            *reinterpret_cast<uint4*>(a_ + i_ * RP * A_LD) = and4(sa[i_], amask);             \
     } while (0)
 
     f32x16 acc[MT][NC];
@@ -206,10 +200,20 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
             if (kb < nblk) {
                 const int buf = kb & 1;
                 const uint16_t* as = As[buf] + li * A_LD + 8 * kg;
+                // the A fragments of k-step ks+1 are read from LDS while the
+                // matrix cores work on k-step ks
+                bf16x8 af[2][MT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t) af[0][t] = *reinterpret_cast<const bf16x8*>(as + t * 32 * A_LD);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int step = kb * KS + ks;
                     const int slot = h * KS + ks;
+                    if (ks + 1 < KS) {
+#pragma unroll
+                        for (int t = 0; t < MT; ++t)
+                            af[(ks + 1) & 1][t] = *reinterpret_cast<const bf16x8*>(as + t * 32 * A_LD + (ks + 1) * 16);
+                    }
                     bf16x8 bc[NC];
 #pragma unroll
                     for (int c = 0; c < NC; ++c) {
@@ -218,12 +222,10 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
                     }
                     if (step < nsteps) {
 #pragma unroll
-                        for (int t = 0; t < MT; ++t) {
-                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + t * 32 * A_LD + ks * 16);
+                        for (int t = 0; t < MT; ++t)
 #pragma unroll
                             for (int c = 0; c < NC; ++c)
-                                acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bc[c], acc[t][c], 0, 0, 0);
-                        }
+                                acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][t], bc[c], acc[t][c], 0, 0, 0);
                     }
                 }
                 // block kb+1 (in registers) into the other buffer; every wave
