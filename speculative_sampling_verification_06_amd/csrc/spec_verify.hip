@@ -363,21 +363,41 @@ __device__ __forceinline__ AmState block_reduce_am(AmState v, AmState* sh)
     return r;
 }
 
-__device__ __forceinline__ float wave_sum(float v)
+// Cross-lane moves within the wave by DPP (data-parallel primitives: a VALU
+// operand modifier, no LDS round trip as with ds_bpermute).  Lanes whose
+// source is outside the pattern, or rows the mask leaves out, read 0.
+// gfx9 DPP controls: quad_perm 0x00-0xFF, row_shr:n 0x110+n, row_mirror
+// 0x140, row_half_mirror 0x141, row_bcast:15 0x142, row_bcast:31 0x143.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
+                                                                 false));
 }
 
+// Sum over the wave in a fixed order (pairs, quads, half rows, rows, then
+// rows 0+1 and 2+3, then the two halves); every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<0xb1>(v);                  // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4e>(v);                  // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp<0x141>(v);                 // row_half_mirror: the other quad of the half row
+    v += dpp<0x140>(v);                 // row_mirror: the other half of the row
+    v += dpp<0x142, 0xa>(v);            // rows 1, 3 += last lane of rows 0, 2
+    v += dpp<0x143, 0xc>(v);            // rows 2, 3 += lane 31 (rows 0 + 1)
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Inclusive scan over the wave (lane order): within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8, then the rows' totals carried forward.
 __device__ __forceinline__ float wave_incl_scan(float v)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(v, off, 64);
-        if (lane >= off) v += y;
-    }
+    v += dpp<0x111>(v);                 // row_shr:1
+    v += dpp<0x112>(v);                 // row_shr:2
+    v += dpp<0x114>(v);                 // row_shr:4
+    v += dpp<0x118>(v);                 // row_shr:8
+    v += dpp<0x142, 0xa>(v);            // rows 1, 3 += total of rows 0, 2
+    v += dpp<0x143, 0xc>(v);            // rows 2, 3 += total of rows 0, 1
     return v;
 }
 
