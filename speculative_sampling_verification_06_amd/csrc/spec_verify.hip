@@ -313,26 +313,60 @@ __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t 
 
 // ------------------------------------------------------- block reductions --
 
-// Butterfly over the wave; lane 0 holds the reduction in a fixed order.
+// Cross-lane moves within the wave by DPP (data-parallel primitives: a VALU
+// operand modifier, no LDS round trip as with ds_bpermute).  Lanes whose
+// source is outside the pattern, or rows the mask leaves out, read 0.
+// gfx9 DPP controls: quad_perm 0x00-0xFF, row_shr:n 0x110+n, row_mirror
+// 0x140, row_half_mirror 0x141, row_bcast:15 0x142, row_bcast:31 0x143.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int v, int old)
+{
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float v, float old = 0.f)
+{
+    return __builtin_bit_cast(float, dpp_i<CTRL, ROW_MASK>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, old)));
+}
+// lane l's value on every lane (l uniform over the wave)
+__device__ __forceinline__ float lane_f(float v, int l)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// The reduction order every cross-lane merge below uses: lane ^ 1, lane ^ 2,
+// the other quad of the half row, the other half of the row, rows 0 + 1 and
+// 2 + 3, then the two halves; the result is lane 63's, read by every lane.
+// A lane whose partner a row broadcast leaves out merges the identity.
+
+// Softmax states {max, sum} merged over the wave.
 __device__ __forceinline__ SmState wave_reduce_sm(SmState v, float s)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        SmState o = {__shfl_xor(v.m, off, 64), __shfl_xor(v.z, off, 64)};
-        v = sm_merge(v, o, s);
-    }
-    return v;
+    v = sm_merge(v, {dpp<0xb1>(v.m, NEG_INF), dpp<0xb1>(v.z)}, s);
+    v = sm_merge(v, {dpp<0x4e>(v.m, NEG_INF), dpp<0x4e>(v.z)}, s);
+    v = sm_merge(v, {dpp<0x141>(v.m, NEG_INF), dpp<0x141>(v.z)}, s);
+    v = sm_merge(v, {dpp<0x140>(v.m, NEG_INF), dpp<0x140>(v.z)}, s);
+    v = sm_merge(v, {dpp<0x142, 0xa>(v.m, NEG_INF), dpp<0x142, 0xa>(v.z)}, s);
+    v = sm_merge(v, {dpp<0x143, 0xc>(v.m, NEG_INF), dpp<0x143, 0xc>(v.z)}, s);
+    return {lane_f(v.m, 63), lane_f(v.z, 63)};
 }
 
+// Greedy states {max, lowest index of the max, invalid flag} merged over the
+// wave (the merge is symmetric, so the order only fixes the work).
 __device__ __forceinline__ AmState wave_reduce_am(AmState v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        AmState o = {__shfl_xor(v.v, off, 64), __shfl_xor(v.i, off, 64),
-                     (uint32_t)__shfl_xor((int)v.bad, off, 64)};
-        v = am_merge(v, o);
-    }
-    return v;
+#define SV_AM_STEP(CTRL, MASK)                                                                     \
+    v = am_merge(v, {dpp<CTRL, MASK>(v.v, NEG_INF), dpp_i<CTRL, MASK>(v.i, INT_MAX),              \
+                     (uint32_t)dpp_i<CTRL, MASK>((int)v.bad, 0)})
+    SV_AM_STEP(0xb1, 0xf);
+    SV_AM_STEP(0x4e, 0xf);
+    SV_AM_STEP(0x141, 0xf);
+    SV_AM_STEP(0x140, 0xf);
+    SV_AM_STEP(0x142, 0xa);
+    SV_AM_STEP(0x143, 0xc);
+#undef SV_AM_STEP
+    return {lane_f(v.v, 63), lane_i(v.i, 63), (uint32_t)lane_i((int)v.bad, 63)};
 }
 
 // Workgroup of BT threads; sh holds BT/64 states.  Every thread returns the
@@ -361,18 +395,6 @@ __device__ __forceinline__ AmState block_reduce_am(AmState v, AmState* sh)
 #pragma unroll
     for (int w = 1; w < BT / 64; ++w) r = am_merge(r, sh[w]);
     return r;
-}
-
-// Cross-lane moves within the wave by DPP (data-parallel primitives: a VALU
-// operand modifier, no LDS round trip as with ds_bpermute).  Lanes whose
-// source is outside the pattern, or rows the mask leaves out, read 0.
-// gfx9 DPP controls: quad_perm 0x00-0xFF, row_shr:n 0x110+n, row_mirror
-// 0x140, row_half_mirror 0x141, row_bcast:15 0x142, row_bcast:31 0x143.
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf,
-                                                                 false));
 }
 
 // Sum over the wave in a fixed order (pairs, quads, half rows, rows, then
@@ -462,8 +484,10 @@ __device__ __forceinline__ int64_t chunk_len(int V, int C)
     return ((n8 + C - 1) / C) * 8;
 }
 
+// Six waves per SIMD for the bf16 row streams (80 registers): the merges at
+// the end would otherwise cost a wave per SIMD for a few registers.
 template <int DTT, int DTD>
-__global__ __launch_bounds__(NT) void k_rowstats(const Params P)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_rowstats(const Params P)
 {
     const int K = P.K, R = 2 * K + 1;
     const int per_seq = R * P.C;
@@ -769,7 +793,7 @@ __device__ bool reaches(const Params& P, int b, int j, bool greedy)
 }
 
 template <int DTT, int DTD>
-__global__ __launch_bounds__(NT) void k_rowstats_lazy(const Params P, const int j)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_rowstats_lazy(const Params P, const int j)
 {
     const int K = P.K, R = 2 * K + 1;
     const int Rj = j < K ? 2 : 1;
@@ -1029,7 +1053,7 @@ __device__ int walk_segment(const char* trow, const char* drow, int V, const Pic
     const uint64_t m = pk.overrun ? 0ull : __ballot(cand >= 0);
     if (m) {
         const int L = __ffsll((unsigned long long)m) - 1;
-        return (int)((int64_t)g * SEG + (int64_t)L * LE + __shfl(cand, L, 64));
+        return (int)((int64_t)g * SEG + (int64_t)L * LE + lane_i(cand, L));
     }
     int lastk = -1;
 #pragma unroll
@@ -1037,7 +1061,7 @@ __device__ int walk_segment(const char* trow, const char* drow, int V, const Pic
         if (wv[k] > 0.f) lastk = k;
     const uint64_t mp = __ballot(lastk >= 0);
     const int L = mp ? 63 - __clzll((long long)mp) : 0;
-    const int kk = __shfl(lastk, L, 64);
+    const int kk = lane_i(lastk, L);
     return (int)((int64_t)g * SEG + (int64_t)L * LE + (kk < 0 ? 0 : kk));
 }
 
@@ -1706,20 +1730,20 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         const float mp = lane < G ? __uint_as_float(v[1]) : 0.f;
         // every lane walks the member totals in member order (same bits on all)
         float S = 0.f;
-        for (int l = 0; l < G; ++l) S += __shfl(mr, l, 64);
+        for (int l = 0; l < G; ++l) S += lane_f(mr, l);
         int mode = bonus ? 1 : 0;
         const bool use_p = !(S > 0.f);             // residual rounded to nothing: draw from p_n
         if (use_p) {
             mode = 2;
             S = 0.f;
-            for (int l = 0; l < G; ++l) S += __shfl(mp, l, 64);
+            for (int l = 0; l < G; ++l) S += lane_f(mp, l);
         }
         const float mine = use_p ? mp : mr;
         const float thr = dec.u * S;
         int gs = -1, over = 0;
         float cum = 0.f, lo = 0.f;
         for (int l = 0; l < G; ++l) {
-            const float v2 = __shfl(mine, l, 64);
+            const float v2 = lane_f(mine, l);
             if (gs < 0) {
                 if (v2 > 0.f && cum + v2 > thr) {
                     gs = l;
@@ -1732,7 +1756,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         if (gs < 0) {                              // rounding overrun: the last slice with weight
             over = 1;
             for (int l = G - 1; l >= 0; --l) {
-                const float v2 = __shfl(mine, l, 64);
+                const float v2 = lane_f(mine, l);
                 if (gs < 0 && v2 > 0.f) gs = l;
             }
         }
