@@ -296,7 +296,7 @@ int sv_set_seq_groups(int groups);
 int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
 
 /* Every wait of the SV_MODE_SEQ exchange is bounded: after this many polls
- * (each one load round trip, about 0.5-1 us, so the default bounds a wait
+ * (each one load round trip, about 1 us, so the default bounds a wait
  * at roughly a second) it gives up and the sequence reports accepted_len -1
  * instead of hanging, e.g. when other work keeps some of the call's
  * workgroups from running at the same time: a launch of this schedule
