@@ -17,14 +17,14 @@
 //                    keep an online softmax state (running max m and sum z of
 //                    exp2(x*s - m*s), s = log2(e)/T), greedy rows a
 //                    lowest-index argmax; one 16-byte partial per chunk.
-//   k_decide         one workgroup per sequence: merges the partials in chunk
-//                    order, runs the K tests on wave 0 and finds the first
-//                    rejection n with one ballot; writes accepted_len, the
-//                    accepted prefix, the greedy token, the diagnostics and a
-//                    record for the draw.
-//   k_tiles          one workgroup per (sampling sequence, vocab tile): draw
-//                    weights of row n (residual max(0, p - q) scaled by Z_p, or
-//                    p for the bonus) summed per 512-element segment.
+//   k_tiles          one workgroup per (sequence, vocab tile).  Each merges
+//                    its sequence's partials in chunk order, runs the K tests
+//                    on wave 0 and finds the first rejection n with one
+//                    ballot (tile 0 writes accepted_len, the accepted prefix,
+//                    the greedy token, the diagnostics and a record for the
+//                    search); sampling sequences then sum the draw weights of
+//                    row n (residual max(0, p - q) scaled by Z_p, or p for the
+//                    bonus) per 512-element segment.
 //   k_search         one workgroup per sampling sequence: scans the segment
 //                    sums for u*S, re-reads that one segment, walks it.
 //
@@ -79,7 +79,7 @@ struct Partial {      // one (row, chunk): softmax {m, z} or argmax {m = value, 
     uint32_t bad;
 };
 
-struct SeqRec {       // what k_decide leaves for k_tiles and k_search
+struct SeqRec {       // what tile 0 of k_tiles leaves for k_search
     int32_t n;
     int32_t status;   // 1 = sampling sequence, valid, draw pending
     float mp, zp;     // target row n
@@ -774,7 +774,7 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
 // A workgroup first settles whether its sequence reaches j: reach[b] (written
 // by launch j-1) says position j-1 was streamed, and thread 0 re-runs the test
 // at j-1 from that position's partials with the same merge and test code
-// k_decide uses, so the two can never disagree.
+// k_tiles uses, so the two can never disagree.
 
 template <int DTT, int DTD>
 __device__ bool reaches(const Params& P, int b, int j, bool greedy)
@@ -856,27 +856,51 @@ __global__ __launch_bounds__(NT) void k_decide(const Params P)
     decide_seq<DTT, DTD>(P, b, greedy, true, &dec);
 }
 
-// k_tiles: one workgroup per (sampling sequence b, vocabulary tile t): the
-// draw weights of row n (residual max(0, p - q) scaled by Z_p, or p for the
-// bonus) summed per segment of 64*8 elements (one per wave iteration).
-template <int DTT, int DTD>
+// k_tiles: one workgroup per (sequence b, vocabulary tile t): the draw
+// weights of row n (residual max(0, p - q) scaled by Z_p, or p for the bonus)
+// summed per segment of 64*8 elements (one per wave iteration).  DECIDE:
+// every workgroup of a sampling sequence first settles the sequence's
+// decision itself (the merge of its partials and the tests, a few
+// microseconds; tile 0 of every sequence writes the outputs and the record
+// k_search reads), in place of a k_decide launch; worth it while the grid
+// fits the device at once, since each workgroup pays the decision.
+// Otherwise the record k_decide left says what to draw.
+template <int DTT, int DTD, bool DECIDE>
 __global__ __launch_bounds__(NT) void k_tiles(const Params P)
 {
     const int b = blockIdx.x / P.tiles;
     const int t = blockIdx.x - b * P.tiles;
-    const SeqRec rec = P.rec[b];
-    if (rec.status != 1) return;                    // greedy, invalid: nothing to draw
+    int n;
+    bool bonus;
+    float mp, zp, mq, zq;
+    int32_t xn;
+    if constexpr (DECIDE) {
+        const bool greedy = P.greedy != nullptr && P.greedy[b] != 0;
+        if (t != 0 && greedy) return;              // nothing to draw, outputs from tile 0
+        __shared__ Decision dec;
+        decide_seq<DTT, DTD>(P, b, greedy, t == 0, &dec);
+        if (greedy || !dec.ok) return;             // uniform across the workgroup
+        n = dec.n;
+        bonus = n == (P.klen ? P.klen[b] : P.K);   // valid sequence: the count is in [0, K]
+        mp = dec.mp; zp = dec.zp; mq = dec.mq; zq = dec.zq;
+        xn = (P.onehot && !bonus) ? P.tokens[(int64_t)b * P.K + n] : -1;
+    } else {
+        const SeqRec rec = P.rec[b];
+        if (rec.status != 1) return;               // greedy, invalid: nothing to draw
+        n = rec.n;
+        bonus = rec.bonus != 0;
+        mp = rec.mp; zp = rec.zp; mq = rec.mq; zq = rec.zq;
+        xn = rec.xn;
+    }
 
     const int V = P.V, nseg = P.nseg;
     const float s = P.s;
-    const int n = rec.n;
-    const bool bonus = rec.bonus != 0;
     const bool oh = P.onehot != 0;
     const char* trow = target_row<DTT>(P, b, n);
     const char* drow = (bonus || oh) ? nullptr : draft_row<DTD>(P, b, n);
-    const float cp = shift_of(rec.mp, s);
-    const float cq = bonus ? 0.f : shift_of(rec.mq, s);
-    const float w = bonus ? 0.f : rec.zp / rec.zq;
+    const float cp = shift_of(mp, s);
+    const float cq = bonus ? 0.f : shift_of(mq, s);
+    const float w = bonus ? 0.f : zp / zq;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
@@ -888,7 +912,7 @@ __global__ __launch_bounds__(NT) void k_tiles(const Params P)
         const int64_t e = (int64_t)seg * SEG + (int64_t)lane * LE;
         load8<DTT>(trow, e, V, t_al, xl[k]);
         if (!bonus) {
-            if (oh) onehot8(e, rec.xn, xd[k]);
+            if (oh) onehot8(e, xn, xd[k]);
             else load8<DTD>(drow, e, V, d_al, xd[k]);
         }
     }
@@ -2088,12 +2112,42 @@ static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
     }
 }
 
+// Workgroups of k_tiles<DTT, DTD, true> the current device holds at once,
+// cached per device (0 if the query fails: then the separate decision launch
+// is used, and the failed query leaves no error behind).
+template <int DTT, int DTD>
+static int64_t tiles_capacity()
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    static std::atomic<int> cache[64];
+    static std::atomic<bool> init[64];
+    if (init[dev].load(std::memory_order_acquire)) return cache[dev].load(std::memory_order_relaxed);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_tiles<DTT, DTD, true>),
+                                                     NT, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+    init[dev].store(true, std::memory_order_release);
+    return cus * per_cu;
+}
+
 template <int DTT, int DTD>
 static void launch_draw_t(const Params& P, const Plan& pl, hipStream_t st)
 {
     if (pl.sched == SEQ) return;                   // k_seq already drew
-    hipLaunchKernelGGL((k_decide<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
-    hipLaunchKernelGGL((k_tiles<DTT, DTD>), dim3((unsigned)((int64_t)P.B * pl.tiles)), dim3(NT), 0, st, P);
+    const int64_t nt = (int64_t)P.B * pl.tiles;
+    if (nt <= tiles_capacity<DTT, DTD>()) {
+        hipLaunchKernelGGL((k_tiles<DTT, DTD, true>), dim3((unsigned)nt), dim3(NT), 0, st, P);
+    } else {
+        hipLaunchKernelGGL((k_decide<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
+        hipLaunchKernelGGL((k_tiles<DTT, DTD, false>), dim3((unsigned)nt), dim3(NT), 0, st, P);
+    }
     hipLaunchKernelGGL((k_search<DTT, DTD>), dim3((unsigned)P.B), dim3(NT), 0, st, P);
 }
 
