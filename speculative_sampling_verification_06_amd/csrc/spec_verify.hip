@@ -1394,7 +1394,13 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
 constexpr int GT = 256;               // threads per workgroup
 constexpr int GW = GT / 64;
 constexpr int GU = 3;                 // 16-byte loads in flight per lane and row
-constexpr int GDV = 8;                // draw: 16-byte pieces in flight per lane
+// Draw: 16-byte pieces in flight per lane.  With proposals (K > 0) most
+// draws run while the long chains of positions are still streaming, and a
+// shallower draw leaves those latency-bound streams more of HBM (-1.6 % on
+// the step at B=256, V=152064); at K = 0 every sequence draws at once and the
+// deeper draw is the faster one.
+constexpr int GDV_CHAIN = 4;
+constexpr int GDV_ALONE = 8;
 // Wave priorities (s_setprio): position 0 of every sequence streams with a
 // fair share (3 falling to 0 with progress); a sequence past it is on its way
 // to a decision and maybe a long chain of positions, ahead of every stream of
@@ -1482,7 +1488,7 @@ __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t e
 // used, kept as raw 16-byte pieces (half the registers of unpacked floats);
 // a partial last segment or unaligned rows go one segment per wave at a
 // time.  Per element the arithmetic and its order are the walk's.
-template <int DTT, int DTD, bool OH, bool BONUS>
+template <int DTT, int DTD, bool OH, bool BONUS, int DV>
 __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, int V, int nseg, int sg0, int nl,
                                           float s, float cp, float cq, float w, int32_t ox, bool fast_rows,
                                           float* seg_r, float* seg_p)
@@ -1490,7 +1496,8 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     constexpr int VT = Fmt<DTT>::BYTES / 2;        // 16-byte pieces per eight elements
     constexpr int VD = Fmt<DTD>::BYTES / 2;
     constexpr bool LD = !BONUS && !OH;             // a draft row to load
-    constexpr int DSEG = GDV / (VT + VD);          // segments per wave step
+    constexpr int DSEG = DV / (VT + VD);           // segments per wave step
+    static_assert(DSEG >= 1, "a wave step covers at least one segment");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool partial = (V % SEG) != 0 && sg0 + nl == nseg && nl > 0;
     const int nfast = fast_rows ? nl - (partial ? 1 : 0) : 0;
@@ -1560,7 +1567,8 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     }
 }
 
-template <int DTT, int DTD, bool OH = false>
+// DV: the draw's 16-byte pieces in flight per lane (GDV_CHAIN or GDV_ALONE).
+template <int DTT, int DTD, bool OH = false, int DV = GDV_CHAIN>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_seqg(const Params P)
 {
     const int G = P.G;
@@ -1731,8 +1739,8 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
     const bool fast_rows = t_al && (bonus || OH || d_al);
     __builtin_amdgcn_s_setprio(PRIO_DRAW);
-    if (bonus) draw_sums<DTT, DTD, OH, true>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
-    else draw_sums<DTT, DTD, OH, false>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
+    if (bonus) draw_sums<DTT, DTD, OH, true, DV>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
+    else draw_sums<DTT, DTD, OH, false, DV>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
     __syncthreads();
     float tr = 0.f, tp = 0.f;                      // slice totals, in the scan order the search uses
     for (int base = 0; base < nl; base += GT) {
@@ -1883,7 +1891,8 @@ static int group_max(int32_t B)
 }
 
 // k_seqg workgroups the current device holds at once, per storage-type pair
-// (0 when unknown: the grouped launch is then not used).
+// (0 when unknown: the grouped launch is then not used); the smaller of the
+// two draw depths' counts, so either instance's grid is resident.
 template <int DTT, int DTD, bool OH>
 static int group_capacity_t()
 {
@@ -1895,12 +1904,16 @@ static int group_capacity_t()
     static std::atomic<int> cache[64];
     static std::atomic<bool> init[64];
     if (init[dev].load(std::memory_order_acquire)) return cache[dev].load(std::memory_order_relaxed);
+    int per_cu2 = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH>), GT,
-                                                     0) != hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_CHAIN>), GT, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu2, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_ALONE>), GT, 0) != hipSuccess) {
         (void)hipGetLastError();                   // unknown capacity: one workgroup per sequence
         return 0;
     }
+    if (per_cu2 < per_cu) per_cu = per_cu2;
     cache[dev].store(cus * per_cu, std::memory_order_relaxed);
     init[dev].store(true, std::memory_order_release);
     return cus * per_cu;
@@ -2091,11 +2104,13 @@ static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
         const dim3 gg((unsigned)(group_slots(P.B) * pl.G));
         if (P.onehot) {                            // one storage type: no draft logits
             if constexpr (DTT == DTD) {
-                if (pl.G >= 2) hipLaunchKernelGGL((k_seqg<DTT, DTT, true>), gg, dim3(GT), 0, st, P);
-                else hipLaunchKernelGGL((k_seq<DTT, DTT, true>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
+                if (pl.G < 2) hipLaunchKernelGGL((k_seq<DTT, DTT, true>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
+                else if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_CHAIN>), gg, dim3(GT), 0, st, P);
+                else hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_ALONE>), gg, dim3(GT), 0, st, P);
             }
         } else if (pl.G >= 2) {
-            hipLaunchKernelGGL((k_seqg<DTT, DTD>), gg, dim3(GT), 0, st, P);
+            if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_CHAIN>), gg, dim3(GT), 0, st, P);
+            else hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_ALONE>), gg, dim3(GT), 0, st, P);
         } else {
             hipLaunchKernelGGL((k_seq<DTT, DTD>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
         }
