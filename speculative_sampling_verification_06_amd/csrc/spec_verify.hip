@@ -1394,13 +1394,16 @@ __global__ __launch_bounds__(QT) void k_seq(const Params P)
 constexpr int GT = 256;               // threads per workgroup
 constexpr int GW = GT / 64;
 constexpr int GU = 3;                 // 16-byte loads in flight per lane and row
-// Draw: 16-byte pieces in flight per lane.  With proposals (K > 0) most
-// draws run while the long chains of positions are still streaming, and a
-// shallower draw leaves those latency-bound streams more of HBM (-1.6 % on
-// the step at B=256, V=152064); at K = 0 every sequence draws at once and the
-// deeper draw is the faster one.
-constexpr int GDV_CHAIN = 4;
-constexpr int GDV_ALONE = 8;
+// Draw: 16-byte pieces in flight per lane.  With proposals (K > 0) the
+// sequences that reject at their first position draw while the few long
+// chains of positions are still streaming; those draws go shallow and paced
+// (GDV_EARLY pieces, DRAW_PACE x 64 cycles of sleep per wave step), which
+// leaves the latency-bound chains more of HBM, and finish well before the
+// chains do.  Every other draw, and every draw at K = 0 (all sequences draw
+// at once, nothing else streams), goes deep (GDV_DEEP).
+constexpr int GDV_EARLY = 2;
+constexpr int GDV_DEEP = 8;
+constexpr int DRAW_PACE = 16;
 // Wave priorities (s_setprio): position 0 of every sequence streams with a
 // fair share (3 falling to 0 with progress); a sequence past it is on its way
 // to a decision and maybe a long chain of positions, ahead of every stream of
@@ -1496,8 +1499,7 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     constexpr int VT = Fmt<DTT>::BYTES / 2;        // 16-byte pieces per eight elements
     constexpr int VD = Fmt<DTD>::BYTES / 2;
     constexpr bool LD = !BONUS && !OH;             // a draft row to load
-    constexpr int DSEG = DV / (VT + VD);           // segments per wave step
-    static_assert(DSEG >= 1, "a wave step covers at least one segment");
+    constexpr int DSEG = DV / (VT + VD) > 0 ? DV / (VT + VD) : 1;   // segments per wave step
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool partial = (V % SEG) != 0 && sg0 + nl == nseg && nl > 0;
     const int nfast = fast_rows ? nl - (partial ? 1 : 0) : 0;
@@ -1541,6 +1543,7 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
                 seg_p[l0 + k] = sp;
             }
         }
+        if constexpr (DV == GDV_EARLY) __builtin_amdgcn_s_sleep(DRAW_PACE);
     }
     const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
@@ -1567,8 +1570,9 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     }
 }
 
-// DV: the draw's 16-byte pieces in flight per lane (GDV_CHAIN or GDV_ALONE).
-template <int DTT, int DTD, bool OH = false, int DV = GDV_CHAIN>
+// DV: the draw's 16-byte pieces in flight per lane after a rejection at the
+// first position (GDV_EARLY with proposals, GDV_DEEP at K = 0).
+template <int DTT, int DTD, bool OH = false, int DV = GDV_EARLY>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_seqg(const Params P)
 {
     const int G = P.G;
@@ -1739,8 +1743,14 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
     const bool fast_rows = t_al && (bonus || OH || d_al);
     __builtin_amdgcn_s_setprio(PRIO_DRAW);
-    if (bonus) draw_sums<DTT, DTD, OH, true, DV>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
-    else draw_sums<DTT, DTD, OH, false, DV>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
+    if (bonus)
+        draw_sums<DTT, DTD, OH, true, GDV_DEEP>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r,
+                                                seg_p);
+    else if (n == 0)
+        draw_sums<DTT, DTD, OH, false, DV>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r, seg_p);
+    else
+        draw_sums<DTT, DTD, OH, false, GDV_DEEP>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r,
+                                                 seg_p);
     __syncthreads();
     float tr = 0.f, tp = 0.f;                      // slice totals, in the scan order the search uses
     for (int base = 0; base < nl; base += GT) {
@@ -1907,9 +1917,9 @@ static int group_capacity_t()
     int per_cu2 = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_CHAIN>), GT, 0) != hipSuccess ||
+            &per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_EARLY>), GT, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu2, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_ALONE>), GT, 0) != hipSuccess) {
+            &per_cu2, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_DEEP>), GT, 0) != hipSuccess) {
         (void)hipGetLastError();                   // unknown capacity: one workgroup per sequence
         return 0;
     }
@@ -2105,12 +2115,12 @@ static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
         if (P.onehot) {                            // one storage type: no draft logits
             if constexpr (DTT == DTD) {
                 if (pl.G < 2) hipLaunchKernelGGL((k_seq<DTT, DTT, true>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
-                else if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_CHAIN>), gg, dim3(GT), 0, st, P);
-                else hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_ALONE>), gg, dim3(GT), 0, st, P);
+                else if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_EARLY>), gg, dim3(GT), 0, st, P);
+                else hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_DEEP>), gg, dim3(GT), 0, st, P);
             }
         } else if (pl.G >= 2) {
-            if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_CHAIN>), gg, dim3(GT), 0, st, P);
-            else hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_ALONE>), gg, dim3(GT), 0, st, P);
+            if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_EARLY>), gg, dim3(GT), 0, st, P);
+            else hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_DEEP>), gg, dim3(GT), 0, st, P);
         } else {
             hipLaunchKernelGGL((k_seq<DTT, DTD>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
         }
