@@ -1490,7 +1490,10 @@ __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t e
 // the step issued, unconditionally and from in-range addresses, before any is
 // used, kept as raw 16-byte pieces (half the registers of unpacked floats);
 // a partial last segment or unaligned rows go one segment per wave at a
-// time.  Per element the arithmetic and its order are the walk's.
+// time.  Per element the arithmetic and its order are the walk's.  DV: the
+// 16-byte pieces per lane of a wave step (DSEG = DV / pieces per segment, at
+// least one); a GDV_EARLY draw also sleeps DRAW_PACE x 64 cycles after each
+// step.
 template <int DTT, int DTD, bool OH, bool BONUS, int DV>
 __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, int V, int nseg, int sg0, int nl,
                                           float s, float cp, float cq, float w, int32_t ox, bool fast_rows,
