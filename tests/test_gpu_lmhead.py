@@ -127,3 +127,4 @@ def _fused_case(dev):
     rep = parity.compare(w, g, o)
     _log(f"[lmhead] verify parity {rep}")
     assert err.max() < 1e-3
+    assert rep["flagged_mismatch"] == [], rep

@@ -145,6 +145,7 @@ def test_propose_then_verify_full_size(dev, schedule):
     rep = parity.compare(_as_workload(sub, co), {k: v[pick] for k, v in g.items()}, o)
     _log(f"[lookup] full size, 32 sampled sequences: {rep}; GPU acc hist "
          f"{np.bincount(g['accepted_len'][g['accepted_len'] >= 0], minlength=lw.K + 1).tolist()}")
+    assert rep["flagged_mismatch"] == [], rep
 
 
 @pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.MODE_SEQ, 0)], indirect=True,

@@ -446,3 +446,56 @@ def test_lmhead_product_within_fp64_bound_on_general_values():
                 # every nonzero term is larger than that bound: dropping one is caught
                 smallest = min(abs(hv[b, k, i] * wv[i, v]) for i in range(d) if hv[b, k, i] * wv[i, v] != 0)
                 assert d * u * mag < smallest
+
+
+# ---------------------------------------------------------------------------
+# Decision flags: a test near its boundary, and the zero-residual fallback
+# ---------------------------------------------------------------------------
+
+def _grid_u(x):
+    """x rounded to the uniforms' 2^-24 grid (what fp32 storage holds)."""
+    return np.float32(round(x * 2 ** 24) * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("offset,accept,near", [(-5e-6, True, True), (5e-6, False, True),
+                                                (-2e-5, True, False), (2e-5, False, False)])
+def test_test_margin_and_near_flag(offset, accept, near):
+    """alpha = p(x)/q(x) = (1/8)/(1/4) = 1/2 exactly ([QH] "Giải pháp": accept
+    with probability min(1, p/q)); the reported margin is |u - 1/2| and the
+    near-boundary flag is set exactly when it is below 1e-5 (R19)."""
+    p0 = np.array([1 / 8, 3 / 8, 1 / 4, 1 / 4])
+    q0 = np.full(4, 1 / 4)
+    p1 = np.full(4, 1 / 4)
+    u0 = _grid_u(0.5 + offset)
+    w = I.from_probs(np.stack([p0, p1])[None], q0[None, None], np.array([[0]]),
+                     np.array([[u0, np.float32(0.375)]], np.float32))
+    r = oracle.verify(w)
+    assert r.accepted_len[0] == (1 if accept else 0)
+    assert abs(r.test_margin[0, 0] - abs(float(u0) - 0.5)) < 1e-12
+    assert bool(r.flags[0] & oracle.FLAG_TEST_NEAR) == near
+    # the final draw is far from any boundary: bonus C = (1/4, 1/2, ...) or
+    # the residual (0, 1/8, 0, 0), both put u_K = 3/8 inside token 1
+    assert r.out_tokens[0, -1 if accept else 0] == 1
+    assert not r.flags[0] & oracle.FLAG_DRAW_NEAR
+    assert not r.flags[0] & oracle.FLAG_FALLBACK
+
+
+@pytest.mark.parametrize("uK,y", [(0.05, 0), (0.29, 1), (0.31, 3), (0.5, 3), (0.61, 4), (0.95, 4)])
+def test_zero_residual_falls_back_to_p(uK, y):
+    """A draft token with q(x) = p(x) = 0 (R11: alpha = 0, always rejected) on
+    otherwise identical rows: the residual max(0, p - q) is exactly 0, so the
+    draw falls back to p_0 itself (R5), flagged, with S reported as 0.  The
+    token is the textbook inverse CDF of p_0 = (0.1, 0.2, 0, 0.3, 0.4): the
+    first i with C_i > u ([QH] "Chọn token": the die over the table)."""
+    p0 = np.array([0.1, 0.2, 0.0, 0.3, 0.4])
+    rng = np.random.default_rng(5)
+    p1 = rng.dirichlet(np.ones(5))
+    u = np.array([[_grid_u(0.999), _grid_u(uK)]], np.float32)   # the test's u is irrelevant: alpha = 0
+    w = I.from_probs(np.stack([p0, p1])[None], p0[None, None], np.array([[2]]), u)
+    r = oracle.verify(w)
+    assert r.accepted_len[0] == 0
+    assert r.out_tokens[0].tolist() == [y, -1]
+    assert np.searchsorted(np.cumsum(p0), float(u[0, 1]), side="right") == y
+    assert r.flags[0] & oracle.FLAG_FALLBACK
+    assert r.res_mass[0] == 0.0
+    assert r.test_margin[0, 0] == pytest.approx(float(u[0, 0]))    # |u - alpha| with alpha = 0
