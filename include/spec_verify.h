@@ -48,6 +48,8 @@
  *   SV_EWORKSPACE workspace NULL, misaligned (16 B) or smaller than
  *                sv_workspace_bytes().
  *   SV_ELAUNCH   the HIP launch failed.
+ *   SV_ESCRATCH  (spec_verify_noalloc only) the shape needs more workspace
+ *                than the library's static scratch array holds.
  * Per-sequence input faults are reported on the device: a row the method
  * examines that holds NaN or +Inf or is all -Inf, a token outside [0, V), a
  * uniform outside [0, 1) that the method uses, or a sampling sequence with
@@ -75,6 +77,7 @@ extern "C" {
 #define SV_EINVAL     -1
 #define SV_EWORKSPACE -2
 #define SV_ELAUNCH    -3
+#define SV_ESCRATCH   -4
 
 #define SV_MAX_K 63
 #define SV_MAX_NGRAM 64
@@ -126,6 +129,27 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits,
                    int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype,
                    int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs and errors as spec_verify with dtype for both
+ * target and draft logits, minus the workspace: the call uses a static
+ * device array of sv_noalloc_scratch_bytes() (16 MiB) instead, which each
+ * GPU the library runs on holds until the process ends (looked up on the
+ * first call on each device).  The call allocates and frees nothing.
+ * SV_ESCRATCH (nothing launched) when sv_workspace_bytes(B, K, V, dtype)
+ * exceeds that size; SV_ELAUNCH when the array's device address cannot be
+ * obtained (sv_last_hip_error() tells why).  Every call on one GPU shares its
+ * array, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that may overlap on one GPU (several streams, several
+ * threads) race and give undefined results; order them on one stream.   */
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        float temperature, const uint8_t* greedy_flag,
+                        int32_t B, int32_t K, int32_t V, int32_t dtype,
+                        int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+                        void* stream);
+size_t sv_noalloc_scratch_bytes(void);
 
 /* The same call in two parts, for timing and for checking the parts against
  * the whole: sv_stats streams the target rows, and the draft rows of

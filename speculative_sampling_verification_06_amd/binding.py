@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
-SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_ELAUNCH = 0, -1, -2, -3
+SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_ELAUNCH, SV_ESCRATCH = 0, -1, -2, -3, -4
 SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
@@ -25,7 +25,7 @@ EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "s
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups", "sv_set_wait_limit",
            "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
-           "sv_strerror", "sv_version")
+           "spec_verify_noalloc", "sv_noalloc_scratch_bytes", "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
 
 
@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH):
                 fn = getattr(lib, name)
                 fn.restype = C.c_int
                 fn.argtypes = verify_args
+            lib.spec_verify_noalloc.restype = C.c_int
+            lib.spec_verify_noalloc.argtypes = verify_args[:13] + [C.c_void_p]
+            lib.sv_noalloc_scratch_bytes.restype = C.c_size_t
+            lib.sv_noalloc_scratch_bytes.argtypes = []
             lib.spec_verify_ex.restype = C.c_int
             lib.spec_verify_ex.argtypes = verify_args[:10] + [C.c_int32] + verify_args[10:]
             lib.sv_workspace_bytes.restype = C.c_size_t
@@ -267,10 +271,17 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
     dg = None
     if "p_tok" in outputs:
         dg = SvDiag(*[_dev_ptr(outputs[k], k) for k in ("p_tok", "q_tok", "lse_p", "lse_q", "res_mass")])
-    need = lib.sv_workspace_bytes(B, K, V, dt)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    ws = workspace if workspace is not None else get_workspace(need, dev, stream)
+    noalloc = fn_name == "spec_verify_noalloc"
+    if noalloc:
+        if ddt != dt:
+            raise TypeError("spec_verify_noalloc needs one storage type for target and draft logits")
+        ws_args = ()
+    else:
+        need = lib.sv_workspace_bytes(B, K, V, dt)
+        ws = workspace if workspace is not None else get_workspace(need, dev, stream)
+        ws_args = (ws.data_ptr(), ws.numel())
     dts = (dt,) if ddt == dt else (dt, ddt)
     if ddt != dt:
         fn_name = "spec_verify_ex"
@@ -281,7 +292,7 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
         None if greedy is None else greedy.data_ptr(), B, K, V, *dts,
         _dev_ptr(outputs["accepted_len"], "accepted_len", torch.int32, (B,)),
         _dev_ptr(outputs["out_tokens"], "out_tokens", torch.int32, (B, K + 1)),
-        None if dg is None else C.byref(dg), ws.data_ptr(), ws.numel(), stream)
+        None if dg is None else C.byref(dg), *ws_args, stream)
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
     return outputs
@@ -290,6 +301,19 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
 def verify(target, draft, tokens, uniforms, temperature, greedy=None, **kw):
     """spec_verify on torch device tensors -> Outputs(accepted_len, out_tokens[, diagnostics])."""
     return _call("spec_verify", target, draft, tokens, uniforms, temperature, greedy, **kw)
+
+
+def verify_noalloc(target, draft, tokens, uniforms, temperature, greedy=None, **kw):
+    """spec_verify_noalloc: spec_verify with the library's static scratch as its
+    workspace (the library allocates nothing; outputs are allocated here
+    unless passed in `outputs`)."""
+    if "workspace" in kw:
+        raise TypeError("spec_verify_noalloc takes no workspace")
+    return _call("spec_verify_noalloc", target, draft, tokens, uniforms, temperature, greedy, **kw)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().sv_noalloc_scratch_bytes())
 
 
 def stats(target, draft, tokens, uniforms, temperature, greedy=None, **kw):

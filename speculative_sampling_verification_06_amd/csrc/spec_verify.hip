@@ -2234,6 +2234,42 @@ int sv_verify_mixed(const void* target, const void* draft, const int32_t* tokens
 }
 
 namespace sv {
+
+// Scratch of spec_verify_noalloc, for callers that cannot allocate: one
+// call's workspace in a file-scope device array that every GPU the library
+// runs on holds until the process ends.  On the host this name is only a
+// stand-in for the symbol, never a device address: host code uses the
+// address hipGetSymbolAddress gives for the current device, kept per device.
+constexpr size_t SCRATCH_BYTES = (size_t)16 << 20;
+constexpr int SCRATCH_DEVS = 64;
+__device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+// The current device's copy of `scratch`, looked up once per device with
+// that device current (the first spec_verify_noalloc call on it).  Null on
+// failure, with the HIP error kept for sv_last_hip_error().
+static void* scratch_ptr(int* hip_err)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && (dev < 0 || dev >= SCRATCH_DEVS)) e = hipErrorInvalidDevice;
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *hip_err = (int)e;
+        return nullptr;
+    }
+    static std::atomic<void*> ptrs[SCRATCH_DEVS];
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        *hip_err = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        return nullptr;
+    }
+    ptrs[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace sv
 
 // ------------------------------------------------------------------ C ABI --
@@ -2287,6 +2323,37 @@ int spec_verify_ex(const void* target_logits, const void* draft_logits, const in
                            V, target_dtype, draft_dtype, accepted_len, out_tokens, diag, workspace,
                            workspace_bytes, stream, 0);
 }
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const float* uniforms, float temperature, const uint8_t* greedy_flag, int32_t B, int32_t K,
+                        int32_t V, int32_t dtype, int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+                        void* stream)
+{
+    // the workspace is the device's scratch array: the shape must fit it; no
+    // part of the workspace needs initialising, so nothing is cleared
+    const size_t need = sv_workspace_bytes(B, K, V, dtype);
+    if (need > sv::SCRATCH_BYTES) return SV_ESCRATCH;
+    // the host checks of spec_verify first (an aligned stand-in address of
+    // the scratch's size: checked, never dereferenced, nothing launched)
+    alignas(256) static char stand_in[256];
+    const int rc = sv_verify_mixed(target_logits, draft_logits, draft_tokens, uniforms, temperature, greedy_flag,
+                                   B, K, V, dtype, dtype, accepted_len, out_tokens, diag,
+                                   need > 0 ? stand_in : nullptr, need > 0 ? sv::SCRATCH_BYTES : 0, stream, 1);
+    if (rc != SV_OK || need == 0) return rc;
+    void* ws = nullptr;
+    {
+        int err = 0;
+        ws = sv::scratch_ptr(&err);
+        if (!ws) {
+            g_last_hip = err;
+            return SV_ELAUNCH;
+        }
+    }
+    return spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, greedy_flag, B, K, V,
+                       dtype, accepted_len, out_tokens, diag, ws, ws ? sv::SCRATCH_BYTES : 0, stream);
+}
+
+size_t sv_noalloc_scratch_bytes(void) { return sv::SCRATCH_BYTES; }
 
 int sv_draw(SV_ARGS_DECL)
 {
@@ -2397,6 +2464,7 @@ const char* sv_strerror(int code)
     case SV_EINVAL: return "invalid argument (shape, dtype, temperature, pointer or alignment)";
     case SV_EWORKSPACE: return "workspace missing, misaligned or too small";
     case SV_ELAUNCH: return "HIP kernel launch failed";
+    case SV_ESCRATCH: return "shape needs more workspace than the library's static scratch holds (spec_verify_noalloc)";
     default: return "unknown error";
     }
 }

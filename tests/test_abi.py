@@ -221,3 +221,21 @@ def test_seq_group_knob(lib):
     finally:
         lib.sv_set_mode(old)
         binding.set_seq_groups(0)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """spec_verify_noalloc refuses a shape whose workspace exceeds its static
+    scratch before anything is launched (host check only: no GPU needed)."""
+    cap = int(lib.sv_noalloc_scratch_bytes())
+    assert cap == 16 << 20
+    B = 64
+    while lib.sv_workspace_bytes(B, 63, 64, binding.SV_F32) <= cap:
+        B *= 2
+    dummy = C.c_void_p(4096)                       # never dereferenced: rejected on the host
+    rc = lib.spec_verify_noalloc(dummy, dummy, dummy, dummy, C.c_float(1.0), None, B, 63, 64, binding.SV_F32,
+                                 dummy, dummy, None, None)
+    assert rc == binding.SV_ESCRATCH
+    assert "scratch" in binding.strerror(rc)
+    # host argument errors come first as for spec_verify
+    assert lib.spec_verify_noalloc(dummy, dummy, dummy, dummy, C.c_float(-1.0), None, 2, 3, 64, binding.SV_F32,
+                                   dummy, dummy, None, None) == binding.SV_EINVAL
