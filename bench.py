@@ -455,6 +455,8 @@ def main() -> int:
                     help="row-statistics schedule (the library chooses per call under auto)")
     ap.add_argument("--seq-groups", type=int, default=0,
                     help="cap on workgroups per sequence under --mode seq (0: as many as the device holds)")
+    ap.add_argument("--seq-lookahead", type=int, default=-1, choices=[-1, 0, 1, 2],
+                    help="lookahead of --mode seq (-1: by shape)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this size (for PMC byte scaling)")
     args = ap.parse_args()
@@ -480,6 +482,7 @@ def main() -> int:
     binding.set_mode({"auto": binding.MODE_AUTO, "eager": binding.MODE_EAGER, "lazy": binding.MODE_LAZY,
                       "seq": binding.MODE_SEQ}[args.mode])
     binding.set_seq_groups(args.seq_groups)
+    binding.set_seq_lookahead(args.seq_lookahead)
 
     fn = {"lmhead": bench_lmhead, "sample": bench_sample, "kvcommit": bench_kvcommit,
           "lookup": bench_lookup}.get(args.config, bench_verify)

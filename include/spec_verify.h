@@ -285,7 +285,9 @@ int spec_verify_lookup(const void* target_logits, int32_t dtype, const int32_t* 
  * schedule meets the same definition, though float sums taken in another
  * order may settle a draw within rounding of a boundary differently):
  *   SV_MODE_AUTO  per call: SV_MODE_SEQ when position 0 alone streams at
- *                 least 64 MiB (and the vocabulary fits its limit), else lazy
+ *                 least 64 MiB, or at least 16 MiB with K > 0, B <= 64 and
+ *                 bf16 target logits (and the vocabulary fits its limit),
+ *                 else lazy
  *                 when one eager pass would stream at least 64 MiB of logits
  *                 per position (K+1 launches then pay off), else eager
  *   SV_MODE_EAGER one launch streams every row of every position
@@ -318,6 +320,21 @@ int sv_schedule(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t d
  * not run SV_MODE_SEQ), SV_EINVAL for a shape the call would reject.       */
 int sv_set_seq_groups(int groups);
 int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
+
+/* Lookahead of SV_MODE_SEQ (K > 0, several workgroups per sequence): with 1
+ * the workgroups of a sequence stream position j+1 before they settle
+ * position j, which hides the exchange's round trip behind a stream at the
+ * price of one position read past the first rejection (never used; rows past
+ * the rejection still never change the result); with 0 they stream a
+ * position only once the previous one is settled.  sv_set_seq_lookahead:
+ * -1 = by shape (the default: 1 while position 0 alone streams less than
+ * 64 MiB, else 0; the environment variable SV_SEQ_LOOKAHEAD=0|1 sets an
+ * initial override), 0 or 1 to force it; SV_EINVAL otherwise.
+ * sv_seq_lookahead: the lookahead a call of this shape would use now (0 when
+ * it would not run SV_MODE_SEQ with several workgroups per sequence),
+ * SV_EINVAL for a shape the call would reject.                            */
+int sv_set_seq_lookahead(int lookahead);
+int sv_seq_lookahead(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype);
 
 /* Every wait of the SV_MODE_SEQ exchange is bounded: after this many polls
  * (each one load round trip, about 1 us, so the default bounds a wait

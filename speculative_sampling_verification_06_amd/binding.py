@@ -24,6 +24,7 @@ SV_MAX_K = 63
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_packed_bytes", "sv_lmhead_pack", "sv_lmhead",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups", "sv_set_wait_limit",
+           "sv_set_seq_lookahead", "sv_seq_lookahead",
            "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
            "spec_verify_noalloc", "sv_noalloc_scratch_bytes", "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
@@ -113,6 +114,10 @@ def load_library(path: str = LIB_PATH):
             lib.sv_set_seq_groups.argtypes = [C.c_int]
             lib.sv_seq_groups.restype = C.c_int
             lib.sv_seq_groups.argtypes = [C.c_int32] * 5
+            lib.sv_set_seq_lookahead.restype = C.c_int
+            lib.sv_set_seq_lookahead.argtypes = [C.c_int]
+            lib.sv_seq_lookahead.restype = C.c_int
+            lib.sv_seq_lookahead.argtypes = [C.c_int32] * 5
             lib.sv_set_wait_limit.restype = C.c_int
             lib.sv_set_wait_limit.argtypes = [C.c_int32]
             lib.sv_lmhead_packed_bytes.restype = C.c_size_t
@@ -155,6 +160,22 @@ def set_seq_groups(groups: int) -> None:
     rc = load_library().sv_set_seq_groups(int(groups))
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
+
+
+def set_seq_lookahead(lookahead: int) -> None:
+    """Lookahead of MODE_SEQ: -1 = by shape (default), 0 or 1 to force it."""
+    rc = load_library().sv_set_seq_lookahead(int(lookahead))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+
+
+def seq_lookahead(B: int, K: int, V: int, target_dtype: int, draft_dtype=None) -> int:
+    """Lookahead a MODE_SEQ call of this shape would use (0: none, or not MODE_SEQ)."""
+    rc = int(load_library().sv_seq_lookahead(B, K, V, target_dtype,
+                                             target_dtype if draft_dtype is None else draft_dtype))
+    if rc < 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return rc
 
 
 def set_wait_limit(polls: int) -> None:

@@ -1575,13 +1575,23 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
 
 // DV: the draw's 16-byte pieces in flight per lane after a rejection at the
 // first position (GDV_EARLY with proposals, GDV_DEEP at K = 0).
-template <int DTT, int DTD, bool OH = false, int DV = GDV_EARLY>
+// LA: lookahead.  With LA = 0 a member streams position j only once j-1 is
+// settled.  With LA = 1 it streams (and publishes) position j+1 before it
+// gathers the partials of j, so the exchange's round trip and the wait for
+// the sequence's slowest member hide behind a stream; the price is one
+// position streamed past the first rejection (its partial is never used).
+// Worth it where the chain's latency, not HBM, sets the kernel's length.
+template <int DTT, int DTD, bool OH = false, int DV = GDV_EARLY, int LA = 0>
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_seqg(const Params P)
 {
     const int G = P.G;
     const int xcd = (int)(blockIdx.x % XCDS), loc = (int)(blockIdx.x / XCDS);
     const int q = loc / G;
-    const int b = xcd + XCDS * q;                  // members of a sequence share a die
+    // members of a sequence share a die; slot q of die x holds sequence
+    // 8q + (x + q) mod 8, so a pattern over the sequence index with period 2,
+    // 4 or 8 (e.g. every other sequence greedy) is spread over all dies
+    // instead of loading some dies with all the draft rows and draws
+    const int b = XCDS * q + (xcd + q) % XCDS;
     const int g = loc - q * G;
     if (b >= P.B) return;
     const int K = P.K, V = P.V, R = 2 * K + 1;
@@ -1604,8 +1614,8 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
 
     __shared__ RowStat f_rs[MAXR];
     __shared__ TestIn ti[SV_MAX_K + 1];
-    __shared__ SmState sh_t[GW], sh_d[GW];
-    __shared__ AmState sh_a[GW];
+    __shared__ SmState sh_t[2][GW], sh_d[2][GW];   // per wave, two positions in flight
+    __shared__ AmState sh_a[2][GW];
     __shared__ int sh_stop;                        // 0 go on, 1 stop, 2 a wait gave up
     __shared__ Decision dec;
     __shared__ float seg_r[GMAXSEG], seg_p[GMAXSEG];
@@ -1628,50 +1638,58 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const int tw = (GW - 1) * 64;                  // last wave loads the test inputs
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
 
-    int jb = 0;                                    // last position streamed
-    for (int j = 0; j <= Ke; ++j) {
-        jb = j;
-        const char* trow = target_row<DTT>(P, b, j);
-        const bool dj = has_draft && j < K;
-        if (greedy) {
-            SmState sm = {NEG_INF, 0.f};
-            AmState am = {NEG_INF, INT_MAX, 0u};
-            if (e0 < e1) scan_chunk<DTT, true, GT, GU>(trow, e0, e1, s, sm, am);
-            if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
-            am = wave_reduce_am(am);
-            if (lane == 0) sh_a[wave] = am;
-        } else {
-            SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
-            // position 0: every sequence streams at once (fair share); later
-            // positions: the few long sequences, oldest-first is fine
-            const char* drow = dj ? draft_row<DTD>(P, b, j) : nullptr;
-            if (e0 < e1) {
-                if (j == 0) stream_pair<DTT, DTD, GT, GU, true>(trow, drow, e0, e1, s, st, sd);
-                else stream_pair<DTT, DTD, GT, GU>(trow, drow, e0, e1, s, st, sd);
+    // s: last position streamed and published; d: last position settled
+    // (both uniform over the workgroup).  Stream while at most LA positions
+    // are streamed but unsettled, then settle the oldest.
+    // with lookahead the slices are small (few sequences): four loads per lane
+    // and row cover a 16 KB slice in one round trip
+    constexpr int SU = LA > 0 ? 4 : GU;
+    int s_ = -1, d_ = -1;
+    for (;;) {
+        if (s_ < Ke && s_ - d_ <= LA) {
+            const int j = ++s_, bi = j & 1;
+            const char* trow = target_row<DTT>(P, b, j);
+            const bool dj = has_draft && j < K;
+            if (greedy) {
+                SmState sm = {NEG_INF, 0.f};
+                AmState am = {NEG_INF, INT_MAX, 0u};
+                if (e0 < e1) scan_chunk<DTT, true, GT, SU>(trow, e0, e1, s, sm, am);
+                if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
+                am = wave_reduce_am(am);
+                if (lane == 0) sh_a[bi][wave] = am;
+            } else {
+                SmState st = {NEG_INF, 0.f}, sd = {NEG_INF, 0.f};
+                // position 0: every sequence streams at once (fair share); later
+                // positions: the few long sequences, oldest-first is fine
+                const char* drow = dj ? draft_row<DTD>(P, b, j) : nullptr;
+                if (e0 < e1) {
+                    if (j == 0) stream_pair<DTT, DTD, GT, SU, true>(trow, drow, e0, e1, s, st, sd);
+                    else stream_pair<DTT, DTD, GT, SU>(trow, drow, e0, e1, s, st, sd);
+                }
+                if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
+                st = wave_reduce_sm(st, s);
+                if (dj) sd = wave_reduce_sm(sd, s);
+                if (lane == 0) {
+                    sh_t[bi][wave] = st;
+                    sh_d[bi][wave] = sd;
+                }
             }
-            if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
-            st = wave_reduce_sm(st, s);
-            if (dj) sd = wave_reduce_sm(sd, s);
-            if (lane == 0) {
-                sh_t[wave] = st;
-                sh_d[wave] = sd;
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // this member's partial, merged over its waves in order, published
-            if (lane == 0) {
+            __syncthreads();
+            // this member's partial of position j, merged over its waves in
+            // order, published (the buffer bi is rewritten two streams later,
+            // after the barrier that ends the next stream)
+            if (wave == 0 && lane == 0) {
                 uint64_t* w = region + pos_word(K, G, j, g, 0);
                 const int wi = pos_word(K, G, j, g, 0);
                 if (greedy) {
-                    AmState am = sh_a[0];
-                    for (int w2 = 1; w2 < GW; ++w2) am = am_merge(am, sh_a[w2]);
+                    AmState am = sh_a[bi][0];
+                    for (int w2 = 1; w2 < GW; ++w2) am = am_merge(am, sh_a[bi][w2]);
                     put_word(w, word_tag(ep, salt, wi), __float_as_uint(am.v));
                     put_word(w + 1, word_tag(ep, salt, wi + 1), (uint32_t)am.i | (am.bad ? 0x80000000u : 0u));
                 } else {
-                    SmState st = sh_t[0], sd = sh_d[0];
-                    for (int w2 = 1; w2 < GW; ++w2) st = sm_merge(st, sh_t[w2], s);
-                    for (int w2 = 1; w2 < GW; ++w2) sd = sm_merge(sd, sh_d[w2], s);
+                    SmState st = sh_t[bi][0], sd = sh_d[bi][0];
+                    for (int w2 = 1; w2 < GW; ++w2) st = sm_merge(st, sh_t[bi][w2], s);
+                    for (int w2 = 1; w2 < GW; ++w2) sd = sm_merge(sd, sh_d[bi][w2], s);
                     put_word(w, word_tag(ep, salt, wi), __float_as_uint(st.m));
                     put_word(w + 1, word_tag(ep, salt, wi + 1), __float_as_uint(st.z));
                     if (dj) {
@@ -1680,7 +1698,13 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                     }
                 }
             }
-            // all members' partials, merged in lane order on every member
+            if (s_ < Ke && s_ - d_ <= LA) continue;      // stream the next position first
+        }
+        // settle position j = d+1: all members' partials, merged in lane order
+        // on every member
+        const int j = d_ + 1;
+        const bool dj = has_draft && j < K;
+        if (wave == 0) {
             bool ok;
             RowStat t, d = d0;
             const int first = pos_word(K, G, j, lane, 0);
@@ -1719,9 +1743,9 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
             }
         }
         __syncthreads();
+        d_ = j;
         if (sh_stop) break;
     }
-    (void)jb;
     if (sh_stop == 2) {                            // a wait gave up
         if (tid == 0) P.acc[b] = -1;
         return;
@@ -1847,6 +1871,7 @@ struct Plan {
     bool lazy;
     int gmax;         // grouped per-sequence schedule: workgroups per sequence the workspace holds
     int G, gsegs;     // and the ones this call uses (G < 2: one 1024-thread workgroup per sequence)
+    int la;           // grouped schedule: lookahead (positions streamed before the oldest is settled)
     size_t off_rec, off_reach, off_part, off_seg, off_gep, off_slots, total;
 };
 
@@ -1859,6 +1884,22 @@ static std::atomic<int> g_groups{-1};
 static std::atomic<int> g_spin{GSPIN};
 // per-call nonce of the grouped schedule's tags
 static std::atomic<uint32_t> g_nonce{0};
+// lookahead of the grouped schedule: -1 = by shape (sv_set_seq_lookahead;
+// SV_SEQ_LOOKAHEAD in the environment), else 0 or 1
+static std::atomic<int> g_la{-2};
+
+static int la_knob()
+{
+    int m = g_la.load(std::memory_order_relaxed);
+    if (m == -2) {
+        const char* e = getenv("SV_SEQ_LOOKAHEAD");
+        m = (e && (!strcmp(e, "0") || !strcmp(e, "1") || !strcmp(e, "2"))) ? (int)(e[0] - '0') : -1;
+        int expect = -2;
+        g_la.compare_exchange_strong(expect, m);
+        m = g_la.load(std::memory_order_relaxed);
+    }
+    return m;
+}
 
 static int groups_now()
 {
@@ -1917,16 +1958,24 @@ static int group_capacity_t()
     static std::atomic<int> cache[64];
     static std::atomic<bool> init[64];
     if (init[dev].load(std::memory_order_acquire)) return cache[dev].load(std::memory_order_relaxed);
-    int per_cu2 = 0;
+    int per_cu2 = 0, per_cu3 = 0, per_cu4 = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_EARLY>), GT, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu2, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_DEEP>), GT, 0) != hipSuccess) {
+            &per_cu2, reinterpret_cast<const void*>(&k_seqg<DTT, DTD, OH, GDV_DEEP>), GT, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu3, reinterpret_cast<const void*>(OH ? &k_seqg<DTT, DTD, OH, GDV_DEEP>
+                                                       : &k_seqg<DTT, DTD, OH, GDV_DEEP, 1>), GT, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu4, reinterpret_cast<const void*>(OH ? &k_seqg<DTT, DTD, OH, GDV_DEEP>
+                                                       : &k_seqg<DTT, DTD, OH, GDV_DEEP, 2>), GT, 0) != hipSuccess) {
         (void)hipGetLastError();                   // unknown capacity: one workgroup per sequence
         return 0;
     }
     if (per_cu2 < per_cu) per_cu = per_cu2;
+    if (per_cu3 < per_cu) per_cu = per_cu3;
+    if (per_cu4 < per_cu) per_cu = per_cu4;
     cache[dev].store(cus * per_cu, std::memory_order_relaxed);
     init[dev].store(true, std::memory_order_release);
     return cus * per_cu;
@@ -1942,10 +1991,29 @@ static int group_capacity(int32_t dtt, int32_t dtd, bool onehot)
     return group_capacity_t<SV_BF16, SV_F32, false>();
 }
 
+// Bytes position 0 streams: every target row, and draft rows (K > 0).
+static double pos0_bytes(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd)
+{
+    const double bt = dtt == SV_BF16 ? 2 : 4, bd = dtd == SV_BF16 ? 2 : 4;
+    return (double)B * V * (bt + (K > 0 ? bd : 0.0));
+}
+
+// Lookahead of the per-sequence schedule for this shape: 1 while position 0
+// alone streams less than 64 MiB (the chains of positions, not HBM, then set
+// the kernel's length), else 0; sv_set_seq_lookahead overrides.
+static int lookahead_for(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd)
+{
+    const int k = la_knob();
+    if (k >= 0) return k;
+    return pos0_bytes(B, K, V, dtt, dtd) >= 64.0 * (1 << 20) ? 0 : 1;
+}
+
 // Automatic choice.  The per-sequence schedule (one launch, no row past a
 // rejection read, draws overlapping other sequences' streams) wins once
-// position 0 alone streams at least 64 MiB, enough to fill the chip; it
-// needs the vocabulary's segment sums to fit in LDS.  Otherwise lazy mode,
+// position 0 alone streams at least 64 MiB, enough to fill the chip, and
+// with lookahead from 16 MiB for up to 64 sequences of bf16 rows when there
+// are positions to test; it needs the vocabulary's segment sums to fit in
+// LDS.  Otherwise lazy mode,
 // which pays one latency-bound launch per position (5-20 us each on
 // gfx950), wins once the eager stream is long against K+1 such launches: at
 // least 64 MiB of logits per position; else eager.
@@ -1965,7 +2033,13 @@ static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t 
     if (m == SV_MODE_LAZY) return K == 0 ? EAGER : LAZY;
     const double bt = dtt == SV_BF16 ? 2 : 4, bd = dtd == SV_BF16 ? 2 : 4;
     const double mib64 = 64.0 * (1 << 20);
-    if (seq_ok && (double)B * V * (bt + (K > 0 ? bd : 0.0)) >= mib64) return SEQ;
+    const double p0 = pos0_bytes(B, K, V, dtt, dtd);
+    if (seq_ok && p0 >= mib64) return SEQ;
+    // a few long bf16 rows per sequence: the per-sequence schedule with
+    // lookahead (measured: B=64 K=5 V=128256 35 against 41 us eager, B=32
+    // K=8 V=152064 38 against 47 us); not at B=256 over a 19008-token shard
+    // (54 against 46 us) nor for fp32 target rows (57 against 42 us)
+    if (seq_ok && K > 0 && p0 >= mib64 / 4 && B <= 64 && dtt == SV_BF16) return SEQ;
     if (K == 0) return EAGER;
     const double bytes = (double)B * V * ((double)(K + 1) * bt + (double)K * bd);
     return bytes >= (double)(K + 1) * mib64 ? LAZY : EAGER;
@@ -2011,6 +2085,7 @@ static bool make_plan(int32_t B, int32_t K, int32_t V, Sched sched, Plan* pl)
     pl->gmax = group_max(B);
     pl->G = 1;
     pl->gsegs = pl->nseg;
+    pl->la = 0;
     pl->off_gep = o;  o = align_up(o + sizeof(uint32_t) * (size_t)B, 256);
     pl->off_slots = o;
     o = align_up(o + sizeof(uint64_t) * (size_t)B * (size_t)pl->gmax * (((size_t)K + 1) * 4 + 2), 256);
@@ -2096,6 +2171,7 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
         if (G >= 2 && gsegs <= GMAXSEG) {
             pl->G = (int)G;
             pl->gsegs = (int)gsegs;
+            pl->la = onehot ? 0 : lookahead_for(B, K, V, dtt, dtd);
             uint32_t h = 0x811c9dc5u;
             const uint32_t f[7] = {(uint32_t)B, (uint32_t)K, (uint32_t)V, (uint32_t)G, (uint32_t)dtt,
                                    (uint32_t)dtd, (uint32_t)gsegs};
@@ -2122,7 +2198,9 @@ static void launch_rowstats_t(const Params& P, const Plan& pl, hipStream_t st)
                 else hipLaunchKernelGGL((k_seqg<DTT, DTT, true, GDV_DEEP>), gg, dim3(GT), 0, st, P);
             }
         } else if (pl.G >= 2) {
-            if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_EARLY>), gg, dim3(GT), 0, st, P);
+            if (P.K > 0 && pl.la > 1) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_DEEP, 2>), gg, dim3(GT), 0, st, P);
+            else if (P.K > 0 && pl.la > 0) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_DEEP, 1>), gg, dim3(GT), 0, st, P);
+            else if (P.K > 0) hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_EARLY>), gg, dim3(GT), 0, st, P);
             else hipLaunchKernelGGL((k_seqg<DTT, DTD, false, GDV_DEEP>), gg, dim3(GT), 0, st, P);
         } else {
             hipLaunchKernelGGL((k_seq<DTT, DTD>), dim3((unsigned)P.B), dim3(QT), 0, st, P);
@@ -2421,6 +2499,29 @@ int sv_set_seq_groups(int groups)
     if (groups < 0 || groups > sv::GMAXG) return SV_EINVAL;
     sv::g_groups.store(groups, std::memory_order_relaxed);
     return SV_OK;
+}
+
+int sv_set_seq_lookahead(int lookahead)
+{
+    if (lookahead < -1 || lookahead > 2) return SV_EINVAL;
+    sv::g_la.store(lookahead, std::memory_order_relaxed);
+    return SV_OK;
+}
+
+int sv_seq_lookahead(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t draft_dtype)
+{
+    if (B < 1 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(target_dtype) || !sv::dtype_ok(draft_dtype))
+        return SV_EINVAL;
+    if (sv::choose_sched(B, K, V, target_dtype, draft_dtype) != sv::SEQ) return 0;
+    // the plan of a call on dummy (aligned, non-null) pointers, nothing launched
+    sv::Params P;
+    sv::Plan pl;
+    alignas(16) static char dummy[16];
+    const int rc = sv::prepare(dummy, dummy, reinterpret_cast<const int32_t*>(dummy),
+                               reinterpret_cast<const float*>(dummy), 1.f, nullptr, B, K, V, target_dtype,
+                               draft_dtype, reinterpret_cast<int32_t*>(dummy), reinterpret_cast<int32_t*>(dummy),
+                               nullptr, dummy, (size_t)-1, &P, &pl);
+    return rc == 1 ? (pl.G >= 2 && K > 0 ? pl.la : 0) : SV_EINVAL;
 }
 
 int sv_set_wait_limit(int32_t polls)

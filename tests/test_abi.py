@@ -191,7 +191,12 @@ def test_schedule_query(lib):
         assert binding.schedule(2, 3, 1000, bf) == binding.MODE_EAGER
         assert binding.schedule(256, 8, 152064, bf) == binding.MODE_SEQ           # 148 MiB at position 0
         assert binding.schedule(256, 0, 152064, bf) == binding.MODE_SEQ           # sampling step, 74 MiB
-        assert binding.schedule(64, 5, 128256, bf) == binding.MODE_EAGER          # 31 MiB
+        assert binding.schedule(64, 5, 128256, bf) == binding.MODE_SEQ            # 31 MiB, B <= 64, bf16
+        assert binding.schedule(32, 8, 152064, bf) == binding.MODE_SEQ            # 18.6 MiB
+        assert binding.schedule(256, 8, 19008, bf) == binding.MODE_EAGER          # 18.6 MiB but B = 256
+        assert binding.schedule(32, 5, 128256, binding.SV_F32, bf) == binding.MODE_EAGER   # fp32 target rows
+        assert binding.schedule(64, 0, 128256, bf) == binding.MODE_EAGER          # K = 0: no positions to chain
+        assert binding.schedule(16, 5, 128256, bf) == binding.MODE_EAGER          # 7.8 MiB
         assert binding.schedule(64, 8, 2048 * 1024 + 1, bf) == binding.MODE_LAZY  # past the LDS limit
         for bad in ((1, 64, 10, bf), (1, 1, 0, bf), (-1, 1, 10, bf), (1, 1, 10, 7)):
             with pytest.raises(binding.SpecVerifyError):
@@ -239,3 +244,28 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     # host argument errors come first as for spec_verify
     assert lib.spec_verify_noalloc(dummy, dummy, dummy, dummy, C.c_float(-1.0), None, 2, 3, 64, binding.SV_F32,
                                    dummy, dummy, None, None) == binding.SV_EINVAL
+
+
+def test_seq_lookahead_knob(lib):
+    old = lib.sv_get_mode()
+    try:
+        bf = binding.SV_BF16
+        for bad in (-2, 3):
+            with pytest.raises(binding.SpecVerifyError):
+                binding.set_seq_lookahead(bad)
+        for la in (-1, 0, 1, 2):
+            binding.set_seq_lookahead(la)
+        binding.set_seq_lookahead(-1)
+        lib.sv_set_mode(binding.MODE_EAGER)
+        assert binding.seq_lookahead(64, 5, 128256, bf) == 0          # not the per-sequence schedule
+        lib.sv_set_mode(binding.MODE_AUTO)
+        la = binding.seq_lookahead(64, 5, 128256, bf)
+        # with a device: one position of lookahead at this size; without one the
+        # schedule falls back to one workgroup per sequence, which has none
+        assert la == (1 if binding.seq_groups(64, 5, 128256, bf) >= 2 else 0)
+        assert binding.seq_lookahead(256, 8, 152064, bf) == 0          # 148 MiB at position 0: no lookahead
+        with pytest.raises(binding.SpecVerifyError):
+            binding.seq_lookahead(0, 5, 100, bf)
+    finally:
+        lib.sv_set_mode(old)
+        binding.set_seq_lookahead(-1)

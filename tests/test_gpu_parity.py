@@ -260,19 +260,22 @@ def test_gpu_output_law_chi_square(dev):
 
 @pytest.fixture
 def schedule(dev, request):
-    mode, groups = request.param
+    mode, groups, la = (tuple(request.param) + (-1,))[:3]
     binding.set_mode(mode)
     binding.set_seq_groups(groups)
+    binding.set_seq_lookahead(la)
     yield request.param
     binding.set_mode(binding.MODE_AUTO)
     binding.set_seq_groups(0)
+    binding.set_seq_lookahead(-1)
 
 
-# seq: as many workgroups per sequence as the device holds; seq1: one
-# 1024-thread workgroup per sequence
-SCHED = pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.MODE_LAZY, 0), (binding.MODE_SEQ, 0),
-                                             (binding.MODE_SEQ, 1)],
-                                indirect=True, ids=["eager", "lazy", "seq", "seq1"])
+# seq: as many workgroups per sequence as the device holds, each position
+# settled before the next is streamed; seqla: the same with one position of
+# lookahead; seq1: one 1024-thread workgroup per sequence
+SCHED = pytest.mark.parametrize("schedule", [(binding.MODE_EAGER, 0), (binding.MODE_LAZY, 0), (binding.MODE_SEQ, 0, 0),
+                                             (binding.MODE_SEQ, 0, 1), (binding.MODE_SEQ, 1)],
+                                indirect=True, ids=["eager", "lazy", "seq", "seqla", "seq1"])
 
 
 @SCHED
@@ -331,7 +334,8 @@ def _subset(w, idx):
                       w.uniforms[idx], w.greedy[idx])
 
 
-def test_seq_wait_give_up_marks_invalid_then_recovers(dev):
+@pytest.mark.parametrize("la", [0, 1], ids=["seq", "seqla"])
+def test_seq_wait_give_up_marks_invalid_then_recovers(dev, la):
     """Every wait of the per-sequence exchange bounded to one poll from the host
     (the kernels still run to the end): each sequence is either reported invalid
     or agrees with the oracle, never a length without its drawn token; the next
@@ -343,8 +347,10 @@ def test_seq_wait_give_up_marks_invalid_then_recovers(dev):
                        draft_sigma=0.4, greedy_mask=mask, name="giveup")
     binding.set_mode(binding.MODE_SEQ)
     binding.set_seq_groups(0)
+    binding.set_seq_lookahead(la)
     try:
         assert binding.seq_groups(w.B, w.K, w.V, w.dtype) >= 2
+        assert binding.seq_lookahead(w.B, w.K, w.V, w.dtype) == la
         ws = torch.zeros(binding.workspace_bytes(w.B, w.K, w.V, w.dtype), dtype=torch.uint8, device=dev)
         o = oracle.verify(w)
         binding.set_wait_limit(1)
@@ -364,6 +370,7 @@ def test_seq_wait_give_up_marks_invalid_then_recovers(dev):
     finally:
         binding.set_wait_limit(0)
         binding.set_mode(binding.MODE_AUTO)
+        binding.set_seq_lookahead(-1)
 
 
 def test_two_streams_at_once(dev):
@@ -406,14 +413,17 @@ def test_lazy_reads_only_reached_rows(dev):
         if n + 1 <= w.K:
             t[b, n + 1:, :] = 0x7FC0
     w2 = I.Workload(w.name, w.B, w.K, w.V, w.dtype, w.T, t, w.draft, w.tokens, w.uniforms, w.greedy)
-    for m, groups in ((binding.MODE_EAGER, 0), (binding.MODE_LAZY, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1)):
+    for m, groups, la in ((binding.MODE_EAGER, 0, -1), (binding.MODE_LAZY, 0, -1), (binding.MODE_SEQ, 0, 0),
+                          (binding.MODE_SEQ, 0, 1), (binding.MODE_SEQ, 1, -1)):
         binding.set_mode(m)
         binding.set_seq_groups(groups)
+        binding.set_seq_lookahead(la)
         try:
             g = run_gpu(w2, dev)
         finally:
             binding.set_mode(binding.MODE_AUTO)
             binding.set_seq_groups(0)
+            binding.set_seq_lookahead(-1)
         parity.compare(w2, g, o)
 
 
