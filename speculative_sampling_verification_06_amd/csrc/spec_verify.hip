@@ -1587,11 +1587,12 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const int G = P.G;
     const int xcd = (int)(blockIdx.x % XCDS), loc = (int)(blockIdx.x / XCDS);
     const int q = loc / G;
-    // members of a sequence share a die; slot q of die x holds sequence
-    // 8q + (x + q) mod 8, so a pattern over the sequence index with period 2,
-    // 4 or 8 (e.g. every other sequence greedy) is spread over all dies
-    // instead of loading some dies with all the draft rows and draws
-    const int b = XCDS * q + (xcd + q) % XCDS;
+    // members of a sequence share a die.  With lookahead (few sequences, 8 or
+    // fewer per die) slot q of die x holds sequence 8q + (x + q) mod 8, so a
+    // pattern over the sequence index with period 2, 4 or 8 (e.g. every other
+    // sequence greedy) is spread over all dies instead of loading some dies
+    // with all the draft rows and draws.  Otherwise slot q holds 8q + x.
+    const int b = LA > 0 ? XCDS * q + (xcd + q) % XCDS : xcd + XCDS * q;
     const int g = loc - q * G;
     if (b >= P.B) return;
     const int K = P.K, V = P.V, R = 2 * K + 1;
