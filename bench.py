@@ -8,25 +8,31 @@ B=256 sequences, K=8 draft tokens, V=152064 vocabulary, bf16 logits, T=1,
 sampling (target ~ N(0,4) + log-Zipf bias, draft = target + N(0,2.5)).
 `--config lmhead` times the fused LM-head workload instead (hidden bf16
 [32, 6, 4096] x W bf16 [4096, 128256] -> fp32 target logits, then the verify
-step against bf16 draft logits; one step = GEMM + verify).
+step against bf16 draft logits; one step = spec_lmhead_verify).
 
-Before the W warmup steps the step runs untimed for --settle-ms (200 ms) of
-wall time, so that the K timed steps see the GPU's steady clock rather than
-its ramp out of idle (without it the LM-head step reads 0.318 ms instead of
-0.278 ms on the host clock; the default workload about 1 % slower).
+Timing.  The step first runs untimed for --settle-ms (200 ms) of wall time,
+so the timed steps see the GPU's steady clock rather than its ramp out of
+idle, then W warm-up steps.  The headline (`ms_per_step`, `value`,
+`roofline`) comes from K cache-flushed steps: before each, 1 GiB is read on
+the launch stream (outside the timed region), so the 256 MB last-level cache
+holds none of the inputs and every byte comes from HBM; HIP events on the
+launch stream bracket each step.  `hot` repeats the measurement with the
+inputs left in the caches by the previous step (K bare steps on the host
+clock, and per-kernel events).
 
-Prints one JSON line: verified logits/s (B*(K+1)*V per second, host clock over
-bare steps), the roofline of the dominant kernel and the fp64 oracle's
-throughput on this host as a CPU baseline.  The dominant kernel depends on the
-schedule the shape gets: under the per-sequence schedule (the default
-workload) the whole step is one launch (k_seqg / k_seq), whose algorithmic
-bytes are the rows the method reaches plus the draw's pass over row n; under
-the eager schedule k_rowstats, every target row and every draft row of
-sampling sequences read once (V*s bytes per row); under the lazy schedule the
-row-statistics launches over the rows reached; for the LM-head workload
-k_lmhead (the weight read once plus the hidden states and the fp32 logits,
-with its MFMA rate beside it).  Each is divided by the kernel's average
-duration from HIP events recorded around it on the launch stream.
+Prints one JSON line: verified logits/s (B*(K+1)*V per second), the roofline
+of the dominant kernel (algorithmic bytes over its event-timed duration), the
+fp64 oracle's throughput on this host as a CPU baseline, parity against the
+oracle, and, for the default workload, the same figures for the other named
+workloads under `workloads` (B=64 K=5 V=128256 bf16 half greedy, the fused
+LM head, B=8 K=4 V=32000 fp32).  The dominant kernel depends on the schedule
+the shape gets: under the per-sequence schedule the whole step is one launch
+(k_seqg / k_seq), whose algorithmic bytes are the rows the method reaches
+plus the draw's pass over row n; under the eager schedule k_rowstats, every
+target row and every draft row of sampling sequences read once (V*s bytes
+per row); under the lazy schedule the row-statistics launches over the rows
+reached; for the LM head k_lmhead (the weight read once, the hidden states,
+the fp32 logits written), with its MFMA rate beside it.
 """
 
 from __future__ import annotations
@@ -86,68 +92,97 @@ def _settle(args, torch, *fns):
             return
 
 
-def _timed(torch, stream, K, first, second):
-    """K steps of first() then second() between two synchronizations, nothing
-    else in between (host ms per step); then K more with HIP events around each
-    part on the launch stream (an event record is a queue packet of its own, so
-    those steps are not the ones the host clock times).  Returns (host ms per
-    step, first ms array, second ms array)."""
-    import numpy as np
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        first()
-        second()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        evs[i][0].record(stream)
-        first()
-        evs[i][1].record(stream)
-        second()
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    a = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
-    b = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
-    return (t1 - t0) * 1e3 / K, a, b
-
-
 FLUSH_NOTE = ("1 GiB read on the launch stream before every step (outside the events): the 256 MB "
               "last-level cache then holds none of the inputs and no dirty lines")
 
 
-def _timed_cold(torch, stream, K, first, second, flush_mib=1024):
-    """K steps of first() then second(), each after reading flush_mib MiB on the
-    same stream so the 256 MB last-level cache holds none of the inputs (a read,
-    not a write: written lines would be written back during the timed part);
-    HIP events around each part (the flush is outside them)."""
+class _Flush:
+    """A 1 GiB read on the launch stream: afterwards the 256 MB last-level
+    cache holds none of the step's inputs (a read, not a write: written lines
+    would be written back during the timed part)."""
+
+    def __init__(self, torch, stream, mib=1024):
+        self.torch = torch
+        self.junk = torch.ones(mib << 18, dtype=torch.float32, device=stream.device)
+        self.sink = torch.empty((), dtype=torch.float32, device=stream.device)
+
+    def __call__(self):
+        self.torch.sum(self.junk, dim=0, out=self.sink)
+
+
+def _cold_steps(torch, stream, K, parts):
+    """K steps, each after a cache flush: HIP events around the whole step
+    (ms array), then K more with events between the parts (list of ms arrays,
+    one per part)."""
     import numpy as np
-    junk = torch.ones(flush_mib << 18, dtype=torch.float32, device=stream.device)
-    sink = torch.empty((), dtype=torch.float32, device=stream.device)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    flush = _Flush(torch, stream)
     torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     for i in range(K):
-        torch.sum(junk, dim=0, out=sink)
-        evs[i][0].record(stream)
-        first()
-        evs[i][1].record(stream)
-        second()
-        evs[i][2].record(stream)
+        flush()
+        ev[i][0].record(stream)
+        for f in parts:
+            f()
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
-    del junk
-    a = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
-    b = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
-    return a, b
+    step = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    n = len(parts)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(K)]
+    for i in range(K):
+        flush()
+        ev[i][0].record(stream)
+        for k, f in enumerate(parts):
+            f()
+            ev[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [np.array([e[k].elapsed_time(e[k + 1]) for e in ev]) for k in range(n)]
+    return step, per
 
 
-def _cold_report(np, dom, rest, nbytes):
-    """Cold-cache figures: medians of the dominant part and the rest, and the
-    dominant part's rate on its algorithmic bytes nbytes."""
-    return {"dominant_median_ms": float(np.median(dom)), "rest_median_ms": float(np.median(rest)),
-            "dominant_mean_ms": float(dom.mean()), "achieved": nbytes / (float(dom.mean()) * 1e-3) / 1e9,
-            "frac": nbytes / (float(dom.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "flush": FLUSH_NOTE}
+def _hot_steps(torch, stream, K, parts):
+    """K bare steps between two synchronizations (host ms per step), then K
+    more with events between the parts (an event record is a queue packet of
+    its own, so those are not the steps the host clock times)."""
+    import numpy as np
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        for f in parts:
+            f()
+    torch.cuda.synchronize()
+    host = (time.perf_counter() - t0) * 1e3 / K
+    n = len(parts)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        for k, f in enumerate(parts):
+            f()
+            ev[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    return host, [np.array([e[k].elapsed_time(e[k + 1]) for e in ev]) for k in range(n)]
+
+
+def _measure(args, torch, stream, parts, steps):
+    """Settle, warm up, then the hot and the cache-flushed timings of one step
+    made of `parts` (callables launched in order on `stream`)."""
+    _settle(args, torch, *parts)
+    for _ in range(args.warmup):
+        for f in parts:
+            f()
+    hot_host, hot_per = _hot_steps(torch, stream, steps, parts)
+    cold_step, cold_per = _cold_steps(torch, stream, steps, parts)
+    return {"hot_host_ms": hot_host, "hot_per": hot_per, "cold_step": cold_step, "cold_per": cold_per}
+
+
+def _roofline(np, nbytes, per_ms, kernel, traffic, extra=None):
+    """Roofline of the dominant kernel: algorithmic bytes over its mean duration."""
+    ms = float(per_ms.mean())
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+         "traffic": traffic, "kernel": kernel, "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms}
+    if extra:
+        r.update(extra)
+    return r
 
 
 def _base_result(w, K, warmup, ms_per_step, dtype_name):
@@ -193,8 +228,9 @@ def _copy_calibration(args, torch, dev):
     del src, dst
 
 
-def bench_verify(args, torch, np, binding, I, dev):
-    w = I.CONFIGS[args.config]()
+def bench_verify(args, torch, np, binding, I, dev, w=None, steps=None):
+    w = I.CONFIGS[args.config]() if w is None else w
+    steps = args.steps if steps is None else steps
     print(f"[bench] workload {w.name}: generated", file=sys.stderr, flush=True)
     d = binding.to_device(w, dev)
     a = (d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], d["greedy"])
@@ -202,14 +238,8 @@ def bench_verify(args, torch, np, binding, I, dev):
     out = call.verify()
     stream = torch.cuda.current_stream(dev)
     _copy_calibration(args, torch, dev)
-    _settle(args, torch, call.stats, call.draw)
-    for _ in range(args.warmup):
-        call.stats()
-        call.draw()
-    ms, stats_ms, draw_ms = _timed(torch, stream, args.steps, call.stats, call.draw)
-    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
-    cold_a, cold_b = _timed_cold(torch, stream, args.steps, call.stats, call.draw)
-    print(f"[bench] timed {args.steps} cold-cache steps", file=sys.stderr, flush=True)
+    t = _measure(args, torch, stream, (call.stats, call.draw), steps)
+    print(f"[bench] {w.name}: timed {steps} hot and {steps} cache-flushed steps", file=sys.stderr, flush=True)
 
     eager = I.eager_bytes(w)
     acc = out["accepted_len"].cpu().numpy()
@@ -220,84 +250,86 @@ def bench_verify(args, torch, np, binding, I, dev):
     # eager: every row once; lazy: the rows reached; seq: the whole step in one
     # launch, so the rows reached plus the draw's second pass over row n
     stats_bytes = I.needed_bytes(w, acc) if seq else (I.reached_bytes(w, acc) if lazy else eager)
-    achieved = stats_bytes / (float(stats_ms.mean()) * 1e-3) / 1e9
-    step_ev = stats_ms + draw_ms
-    res = _base_result(w, args.steps, args.warmup, ms, "f32")
+    ms = float(t["cold_step"].mean())
+    res = _base_result(w, steps, args.warmup, ms, "f32")
     res["config"] = {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "logits": I.DTYPE_NAMES[w.dtype],
                      "temperature": w.T, "greedy_sequences": int(w.greedy.sum()), "seed": w.seed,
                      "verified_logits_per_step": w.verified_logits,
                      "schedule": SCHEDULES[sched]}
     if seq:
         res["config"]["workgroups_per_sequence"] = binding.seq_groups(w.B, w.K, w.V, w.dtype)
+        res["config"]["lookahead"] = binding.seq_lookahead(w.B, w.K, w.V, w.dtype)
     kname = {binding.MODE_EAGER: "k_rowstats", binding.MODE_LAZY: "k_rowstats_lazy",
              binding.MODE_SEQ: "k_seqg" if seq and binding.seq_groups(w.B, w.K, w.V, w.dtype) > 1 else "k_seq"}[sched]
-    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": achieved / HBM_PEAK_GBS,
-                       "traffic": _traffic(kname, w.name, "spec_verify.hip"),
-                       "kernel": {binding.MODE_EAGER: "k_rowstats",
-                                  binding.MODE_LAZY: "k_rowstats_lazy (all K+1 launches of a step)",
-                                  binding.MODE_SEQ: "k_seq/k_seqg (the whole step, draw included)"}[sched],
-                       "algorithmic_bytes_per_launch": stats_bytes,
-                       "avg_launch_ms": float(stats_ms.mean()),
-                       "cold": _cold_report(np, cold_a, cold_b, stats_bytes)}
-    res["timing_ms"] = {"step_events_median": float(np.median(step_ev)),
-                        "step_events_p10": float(np.percentile(step_ev, 10)),
-                        "step_events_p90": float(np.percentile(step_ev, 90)),
-                        "k_rowstats_median": float(np.median(stats_ms)),
-                        "decide_search_median": float(np.median(draw_ms))}
+    kdesc = {binding.MODE_EAGER: "k_rowstats",
+             binding.MODE_LAZY: "k_rowstats_lazy (all K+1 launches of a step)",
+             binding.MODE_SEQ: "k_seq/k_seqg (the whole step, draw included)"}[sched]
+    res["roofline"] = _roofline(np, stats_bytes, t["cold_per"][0], kdesc, _traffic(kname, w.name, "spec_verify.hip"),
+                                {"timing": FLUSH_NOTE})
+    hot = _roofline(np, stats_bytes, t["hot_per"][0], kdesc, None)
+    res["hot"] = {"ms_per_step": t["hot_host_ms"], "value": w.verified_logits / (t["hot_host_ms"] * 1e-3),
+                  "achieved": hot["achieved"], "frac": hot["frac"], "avg_launch_ms": hot["avg_launch_ms"],
+                  "timing": "K bare steps on the host clock; per-kernel events; inputs left in the caches by the previous step"}
+    cs = t["cold_step"]
+    res["timing_ms"] = {"step_median": float(np.median(cs)), "step_p10": float(np.percentile(cs, 10)),
+                        "step_p90": float(np.percentile(cs, 90)),
+                        "stats_median": float(np.median(t["cold_per"][0])),
+                        "draw_median": float(np.median(t["cold_per"][1])),
+                        "hot_stats_median": float(np.median(t["hot_per"][0])),
+                        "hot_draw_median": float(np.median(t["hot_per"][1]))}
     res["method"] = _method_stats(w, acc)
     needed = I.needed_bytes(w, acc)
     res["method"].update(needed_bytes=needed, eager_bytes=eager, useful_bytes_fraction=needed / eager)
     return w, gpu, res, None
 
 
-def bench_lmhead(args, torch, np, binding, I, dev):
-    w = I.cfg_lmhead()
+def bench_lmhead(args, torch, np, binding, I, dev, w=None, steps=None):
+    w = I.cfg_lmhead() if w is None else w
+    steps = args.steps if steps is None else steps
     print(f"[bench] workload {w.name}: generated", file=sys.stderr, flush=True)
     M, d, V = w.B * (w.K + 1), w.hidden.shape[-1], w.V
     hidden = binding.bf16_tensor(w.hidden, dev)
     wt = binding.lmhead_pack(binding.bf16_tensor(w.w_lm, dev))   # static weight, packed once
     dd = binding.to_device(w, dev)
-    logits = torch.empty(w.B, w.K + 1, V, dtype=torch.float32, device=dev)
-    gemm = binding.BoundLMHead(hidden.view(M, d), wt, logits.view(M, V))
-    gemm()
-    call = binding.Bound(logits, dd["draft"], dd["tokens"], dd["uniforms"], w.T, dd["greedy"])
-    out = call.verify()
+    call = binding.BoundLMHeadVerify(hidden, wt, dd["draft"], dd["tokens"], dd["uniforms"], w.T, dd["greedy"])
+    out = call()
     stream = torch.cuda.current_stream(dev)
     _copy_calibration(args, torch, dev)
-    _settle(args, torch, gemm, call.verify)
-    for _ in range(args.warmup):
-        gemm()
-        call.verify()
-    ms, gemm_ms, ver_ms = _timed(torch, stream, args.steps, gemm, call.verify)
-    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    t = _measure(args, torch, stream, (call.gemm, call.rest), steps)
+    print(f"[bench] {w.name}: timed {steps} hot and {steps} cache-flushed steps", file=sys.stderr, flush=True)
 
     acc = out["accepted_len"].cpu().numpy()
-    gpu = {k: v.cpu().numpy() for k, v in out.items()}
+    gpu = {k: v.cpu().numpy() for k, v in out.items() if k != "target_logits"}
     gemm_bytes = V * d * 2 + M * d * 2 + M * V * 4
     flops = 2.0 * M * d * V
-    g_s = float(gemm_ms.mean()) * 1e-3
-    achieved = gemm_bytes / g_s / 1e9
-    res = _base_result(w, args.steps, args.warmup, ms, "bf16-mfma+f32")
+    ms = float(t["cold_step"].mean())
+    res = _base_result(w, steps, args.warmup, ms, "bf16-mfma+f32")
     res["config"] = {"workload": w.name, "B": w.B, "K": w.K, "V": V, "d": d,
-                     "logits": "f32 target / bf16 draft", "temperature": w.T, "seed": w.seed,
-                     "verified_logits_per_step": w.verified_logits}
-    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": achieved / HBM_PEAK_GBS,
-                       "traffic": _traffic("k_lmhead", w.name, "lmhead.hip"),
-                       "kernel": "k_lmhead", "algorithmic_bytes_per_launch": gemm_bytes,
-                       "avg_launch_ms": float(gemm_ms.mean()),
-                       "mfma_tflops": flops / g_s / 1e12,
-                       "mfma_frac": flops / g_s / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-    res["timing_ms"] = {"k_lmhead_median": float(np.median(gemm_ms)),
-                        "verify_median": float(np.median(ver_ms)),
-                        "step_events_median": float(np.median(gemm_ms + ver_ms))}
+                     "logits": "f32 target / bf16 draft",
+                     "temperature": w.T, "seed": w.seed, "verified_logits_per_step": w.verified_logits}
+
+    def mfma(per):
+        g = float(per.mean()) * 1e-3
+        return {"mfma_tflops": flops / g / 1e12, "mfma_frac": flops / g / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    res["roofline"] = _roofline(np, gemm_bytes, t["cold_per"][0], "k_lmhead",
+                                _traffic("k_lmhead", w.name, "lmhead.hip"),
+                                dict(mfma(t["cold_per"][0]), timing=FLUSH_NOTE))
+    hot = _roofline(np, gemm_bytes, t["hot_per"][0], "k_lmhead", None, mfma(t["hot_per"][0]))
+    res["hot"] = {"ms_per_step": t["hot_host_ms"], "value": w.verified_logits / (t["hot_host_ms"] * 1e-3),
+                  "achieved": hot["achieved"], "frac": hot["frac"], "avg_launch_ms": hot["avg_launch_ms"],
+                  "mfma_frac": hot["mfma_frac"],
+                  "timing": "K bare steps on the host clock; per-kernel events; inputs left in the caches by the previous step"}
+    res["timing_ms"] = {"step_median": float(np.median(t["cold_step"])),
+                        "k_lmhead_median": float(np.median(t["cold_per"][0])),
+                        "verify_median": float(np.median(t["cold_per"][1])),
+                        "hot_k_lmhead_median": float(np.median(t["hot_per"][0])),
+                        "hot_verify_median": float(np.median(t["hot_per"][1]))}
     res["method"] = _method_stats(w, acc)
     return w, gpu, res, "lmhead"
 
 
 def _timed_one(torch, stream, K, fn):
-    """As _timed for a one-part step: host ms per step over K bare steps, then
+    """A one-part step: host ms per step over K bare steps, then
     the event-timed ms of K more."""
     import numpy as np
     torch.cuda.synchronize()
@@ -354,14 +386,9 @@ def bench_lookup(args, torch, np, binding, I, dev):
     uni = torch.from_numpy(lw.uniforms).to(dev)
     call = binding.BoundLookup(hist, hl, lw.n_max, lw.n_min, tt, uni, lw.T)
     stream = torch.cuda.current_stream(dev)
-    _settle(args, torch, call.propose, call.verify)
-    for _ in range(args.warmup):
-        call.propose()
-        call.verify()
-    ms, prop_ms, ver_ms = _timed(torch, stream, args.steps, call.propose, call.verify)
-    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
-    cold_p, cold_v = _timed_cold(torch, stream, args.steps, call.propose, call.verify)
-    print(f"[bench] timed {args.steps} cold-cache steps", file=sys.stderr, flush=True)
+    t = _measure(args, torch, stream, (call.propose, call.verify), args.steps)
+    print(f"[bench] {lw.name}: timed {args.steps} hot and {args.steps} cache-flushed steps", file=sys.stderr,
+          flush=True)
     klen = call.klen.cpu().numpy()
     out = call.outputs
     acc = out["accepted_len"].cpu().numpy()
@@ -376,21 +403,23 @@ def bench_lookup(args, torch, np, binding, I, dev):
     w = I.Workload(lw.name, lw.B, lw.K, lw.V, lw.dtype, lw.T, lw.target, np.zeros((lw.B, lw.K, 0), np.uint16),
                    gpu["_cand"], lw.uniforms, lw.greedy, seed=lw.seed)
     w.lookup = lw
-    res = _base_result(w, args.steps, args.warmup, ms, "f32")
+    res = _base_result(w, args.steps, args.warmup, float(t["cold_step"].mean()), "f32")
     res["config"] = {"workload": lw.name, "B": lw.B, "K": lw.K, "V": lw.V, "logits": "bf16",
                      "history_tokens": int(lw.hist_len.sum()), "n_max": lw.n_max, "n_min": lw.n_min,
                      "temperature": lw.T, "seed": lw.seed,
                      "schedule": "automatic for one-hot proposals (per-sequence at this size)"}
-    v_s = float(ver_ms.mean()) * 1e-3
-    res["roofline"] = {"bound": "hbm", "achieved": ver_bytes / v_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": ver_bytes / v_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                       "kernel": "spec_verify_lookup (one launch: k_seqg with one-hot proposals)",
-                       "algorithmic_bytes_per_launch": ver_bytes, "avg_launch_ms": float(ver_ms.mean()),
-                       "proposer_avg_ms": float(prop_ms.mean()), "proposer_history_bytes": hist_bytes,
-                       "proposer_gbs": hist_bytes / (float(prop_ms.mean()) * 1e-3) / 1e9,
-                       "cold": _cold_report(np, cold_v, cold_p, ver_bytes)}
-    res["timing_ms"] = {"propose_median": float(np.median(prop_ms)), "verify_median": float(np.median(ver_ms)),
-                        "step_events_median": float(np.median(prop_ms + ver_ms))}
+    prop_ms = t["cold_per"][0]
+    res["roofline"] = _roofline(np, ver_bytes, t["cold_per"][1],
+                                "spec_verify_lookup (one launch: k_seqg with one-hot proposals)", None,
+                                {"proposer_avg_ms": float(prop_ms.mean()), "proposer_history_bytes": hist_bytes,
+                                 "proposer_gbs": hist_bytes / (float(prop_ms.mean()) * 1e-3) / 1e9,
+                                 "timing": FLUSH_NOTE})
+    hot = _roofline(np, ver_bytes, t["hot_per"][1], "spec_verify_lookup", None)
+    res["hot"] = {"ms_per_step": t["hot_host_ms"], "value": w.verified_logits / (t["hot_host_ms"] * 1e-3),
+                  "achieved": hot["achieved"], "frac": hot["frac"], "avg_launch_ms": hot["avg_launch_ms"]}
+    res["timing_ms"] = {"propose_median": float(np.median(t["cold_per"][0])),
+                        "verify_median": float(np.median(t["cold_per"][1])),
+                        "step_median": float(np.median(t["cold_step"]))}
     res["method"] = _method_stats(w, acc)
     res["method"]["candidates_hist"] = np.bincount(np.maximum(klen, 0), minlength=lw.K + 1).tolist()
     return w, gpu, res, "lookup"
@@ -457,6 +486,10 @@ def main() -> int:
                     help="cap on workgroups per sequence under --mode seq (0: as many as the device holds)")
     ap.add_argument("--seq-lookahead", type=int, default=-1, choices=[-1, 0, 1, 2],
                     help="lookahead of --mode seq (-1: by shape)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="default workload only: skip the other named workloads' figures (`workloads`)")
+    ap.add_argument("--workload-steps", type=int, default=30,
+                    help="timed steps (hot and cache-flushed each) of every other named workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this size (for PMC byte scaling)")
     args = ap.parse_args()
@@ -556,8 +589,46 @@ def main() -> int:
         result["cpu_baseline"] = None
     result["settle_ms"] = args.settle_ms
 
+    if args.config == "cfg152k" and not args.no_workloads:
+        result["workloads"] = {}
+        for name, leg, make in (("cfg128k", bench_verify, I.cfg_128k), ("lmhead", bench_lmhead, I.cfg_lmhead),
+                                ("cfg32k", bench_verify, I.cfg_32k)):
+            wl, gl, rl, kl = leg(args, torch, np, binding, I, dev, w=make(), steps=args.workload_steps)
+            result["workloads"][name] = _summary(rl, _parity(np, wl, gl, kl))
+            print(f"[bench] {name}: {result['workloads'][name]}", file=sys.stderr, flush=True)
+
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _parity(np, w, gpu, kind):
+    """The oracle on the same inputs (no timing) and the parity report."""
+    import oracle
+    from oracle import parity
+    oracle.build(force=False)
+    tgt = oracle.lmhead_logits(w.hidden, w.w_lm) if kind == "lmhead" else None
+    orc = oracle.verify(w, target=tgt)
+    try:
+        rep = parity.compare(w, gpu, orc)
+        return {"ok": True, "flagged": rep["flagged"], "flagged_mismatch": len(rep["flagged_mismatch"]),
+                "invalid": rep["invalid"]}
+    except parity.ParityError as e:
+        return {"ok": False, "error": str(e)[:300]}
+
+
+def _summary(r, par):
+    """The figures of one named workload for the `workloads` entry."""
+    rf, hot = r["roofline"], r["hot"]
+    out = {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"], "value": r["value"],
+           "unit": r["unit"], "dominant_kernel": rf["kernel"], "algorithmic_bytes": rf["algorithmic_bytes_per_launch"],
+           "avg_launch_ms": rf["avg_launch_ms"], "achieved_GBs": rf["achieved"], "roofline_frac": rf["frac"],
+           "hot_ms_per_step": hot["ms_per_step"], "hot_frac": hot["frac"], "timing_ms": r["timing_ms"],
+           "parity": par, "accepted_len_hist": r["method"]["accepted_len_hist"]}
+    if "schedule" in r["config"]:
+        out["schedule"] = r["config"]["schedule"]
+    if "mfma_frac" in rf:
+        out["mfma_frac"] = rf["mfma_frac"]
+    return out
 
 
 if __name__ == "__main__":

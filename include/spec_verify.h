@@ -198,7 +198,11 @@ int sv_draw(const void* target_logits, const void* draft_logits,
  *   target_logits [B, K+1, V] fp32 buffer, then the verify step of
  *   spec_verify on those logits with draft logits of draft_dtype.  Every
  *   check of both parts runs before anything is launched; outputs, errors
- *   and workspace as spec_verify (size it with dtype SV_F32).            */
+ *   and workspace as spec_verify (size it with dtype SV_F32).
+ *   Deviation from a plain w_lm [d, V] argument: the weight is taken packed
+ *   (sv_lmhead_pack, once per static weight), because the GEMM streams it in
+ *   matrix-core operand order (measured 351 -> 271 us for W [4096, 128256]
+ *   against reading rows of W^T directly).                               */
 size_t sv_lmhead_packed_bytes(int32_t d, int32_t V);
 int sv_lmhead_pack(const void* w_dv, void* w_packed, int32_t d, int32_t V, void* stream);
 int sv_lmhead(const void* hidden, const void* w_packed, int32_t M, int32_t d, int32_t V,
@@ -208,6 +212,21 @@ int spec_lmhead_verify(const void* hidden, const void* w_packed, int32_t d, floa
                        const float* uniforms, float temperature, const uint8_t* greedy_flag,
                        int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
                        const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_lmhead_verify in two calls, for timing the parts: _gemm launches the
+ * LM head, _rest the verify step on its logits.  Same arguments and checks
+ * as spec_lmhead_verify; _rest must follow _gemm on the same stream with
+ * identical arguments.                                                    */
+int sv_lmhead_verify_gemm(const void* hidden, const void* w_packed, int32_t d, float* target_logits,
+                          const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
+                          const float* uniforms, float temperature, const uint8_t* greedy_flag,
+                          int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                          const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
+int sv_lmhead_verify_rest(const void* hidden, const void* w_packed, int32_t d, float* target_logits,
+                          const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
+                          const float* uniforms, float temperature, const uint8_t* greedy_flag,
+                          int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                          const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- draft-side sampling step ---------------------------------------------
  * Each draft pass draws its candidate x ~ q = softmax(d / T) ([QH] "Một vòng":

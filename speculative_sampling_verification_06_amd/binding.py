@@ -22,6 +22,7 @@ SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
 EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "sv_draw", "sv_lmhead_packed_bytes", "sv_lmhead_pack", "sv_lmhead",
+           "sv_lmhead_verify_gemm", "sv_lmhead_verify_rest",
            "spec_lmhead_verify", "sv_sample_workspace_bytes", "sv_sample", "sv_kv_commit",
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups", "sv_set_wait_limit",
            "sv_set_seq_lookahead", "sv_seq_lookahead",
@@ -127,11 +128,12 @@ def load_library(path: str = LIB_PATH):
             lib.sv_lmhead.restype = C.c_int
             lib.sv_lmhead.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                       C.c_void_p]
-            lib.spec_lmhead_verify.restype = C.c_int
-            lib.spec_lmhead_verify.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
-                                               C.c_int32, C.c_void_p, C.c_void_p, C.c_float, C.c_void_p,
-                                               C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
-                                               C.POINTER(SvDiag), C.c_void_p, C.c_size_t, C.c_void_p]
+            lmv_args = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                        C.c_void_p, C.c_float, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                        C.c_void_p, C.POINTER(SvDiag), C.c_void_p, C.c_size_t, C.c_void_p]
+            for name in ("spec_lmhead_verify", "sv_lmhead_verify_gemm", "sv_lmhead_verify_rest"):
+                getattr(lib, name).restype = C.c_int
+                getattr(lib, name).argtypes = lmv_args
             _lib = lib
     return _lib
 
@@ -514,10 +516,41 @@ def lmhead(hidden, packed, out=None):
     return out
 
 
+class BoundLMHeadVerify:
+    """spec_lmhead_verify of one problem with pre-marshalled arguments; also
+    its two parts (sv_lmhead_verify_gemm, sv_lmhead_verify_rest) for timing."""
+
+    def __init__(self, hidden, packed, draft, tokens, uniforms, temperature, greedy=None, *, diag=True,
+                 stream=None):
+        torch = _torch()
+        self.outputs, self._args, self._keep = _lmhead_verify_call(hidden, packed, draft, tokens, uniforms,
+                                                                   temperature, greedy, diag=diag, stream=stream)
+        torch.cuda.synchronize(hidden.device)
+        lib = load_library()
+        self._all, self._gemm, self._rest = lib.spec_lmhead_verify, lib.sv_lmhead_verify_gemm, lib.sv_lmhead_verify_rest
+
+    def __call__(self):
+        _check_rc(self._all(*self._args))
+        return self.outputs
+
+    def gemm(self):
+        _check_rc(self._gemm(*self._args))
+
+    def rest(self):
+        _check_rc(self._rest(*self._args))
+        return self.outputs
+
+
 def lmhead_verify(hidden, packed, draft, tokens, uniforms, temperature, greedy=None, *,
                   target_logits=None, diag=True, stream=None):
     """spec_lmhead_verify: the LM-head GEMM into target_logits [B, K+1, V] fp32,
     then the verify step.  Returns Outputs (+ target_logits)."""
+    return _lmhead_verify_call(hidden, packed, draft, tokens, uniforms, temperature, greedy,
+                               target_logits=target_logits, diag=diag, stream=stream)[0]
+
+
+def _lmhead_verify_call(hidden, packed, draft, tokens, uniforms, temperature, greedy=None, *,
+                        target_logits=None, diag=True, stream=None):
     torch = _torch()
     lib = load_library()
     B, K1, d = hidden.shape
@@ -546,15 +579,17 @@ def lmhead_verify(hidden, packed, draft, tokens, uniforms, temperature, greedy=N
         stream = torch.cuda.current_stream(dev).cuda_stream
     ws = get_workspace(lib.sv_workspace_bytes(B, K, V, SV_F32), dev, stream)
     ddt = SV_F32 if draft is None else _dtype_code(draft)
-    _check_rc(lib.spec_lmhead_verify(
-        hidden.data_ptr(), packed.data.data_ptr(), d, target_logits.data_ptr(),
-        None if draft is None else draft.data_ptr(), ddt,
-        None if tokens is None or tokens.numel() == 0 else tokens.data_ptr(), uniforms.data_ptr(),
-        C.c_float(float(temperature)), None if greedy is None else greedy.data_ptr(), B, K, V,
-        o["accepted_len"].data_ptr(), o["out_tokens"].data_ptr(), None if dg is None else C.byref(dg),
-        ws.data_ptr(), ws.numel(), stream))
+    args = (C.c_void_p(hidden.data_ptr()), C.c_void_p(packed.data.data_ptr()), C.c_int32(d),
+            C.c_void_p(target_logits.data_ptr()), C.c_void_p(None if draft is None else draft.data_ptr()),
+            C.c_int32(ddt), C.c_void_p(None if tokens is None or tokens.numel() == 0 else tokens.data_ptr()),
+            C.c_void_p(uniforms.data_ptr()), C.c_float(float(temperature)),
+            C.c_void_p(None if greedy is None else greedy.data_ptr()), C.c_int32(B), C.c_int32(K), C.c_int32(V),
+            C.c_void_p(o["accepted_len"].data_ptr()), C.c_void_p(o["out_tokens"].data_ptr()),
+            None if dg is None else C.byref(dg), C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel()),
+            C.c_void_p(stream))
+    _check_rc(lib.spec_lmhead_verify(*args))
     o["target_logits"] = target_logits
-    return o
+    return o, args, (hidden, packed, draft, tokens, uniforms, greedy, ws, target_logits, dg)
 
 
 def bf16_tensor(bits, device):

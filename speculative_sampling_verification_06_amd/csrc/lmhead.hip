@@ -300,16 +300,22 @@ int sv_lmhead(const void* hidden, const void* w_packed, int32_t M, int32_t d, in
     return sv_launch_status();
 }
 
-int spec_lmhead_verify(const void* hidden, const void* w_packed, int32_t d, float* target_logits,
-                       const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
-                       const float* uniforms, float temperature, const uint8_t* greedy_flag,
-                       int32_t B, int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
-                       const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace svlm {
+
+// spec_lmhead_verify's launches: part 1 the GEMM, part 2 the verify step on
+// its logits, 3 both.  Every host check of both runs first.
+static int lmhead_verify_parts(int parts, const void* hidden, const void* w_packed, int32_t d, float* target_logits,
+                               const void* draft_logits, int32_t draft_dtype, const int32_t* draft_tokens,
+                               const float* uniforms, float temperature, const uint8_t* greedy_flag, int32_t B,
+                               int32_t K, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                               const sv_diag* diag, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (B < 0 || K < 0 || K > SV_MAX_K) return SV_EINVAL;
     if ((int64_t)B * (K + 1) > INT_MAX) return SV_EINVAL;
     const int32_t M = B * (K + 1);
-    int rc = svlm::check_gemm(hidden, w_packed, M, d, V, target_logits);
+    int rc = check_gemm(hidden, w_packed, M, d, V, target_logits);
     if (rc < 0) return rc;
     if (B == 0) return SV_OK;
     // every check of the verify step runs before anything is launched
@@ -317,11 +323,31 @@ int spec_lmhead_verify(const void* hidden, const void* w_packed, int32_t d, floa
                          V, SV_F32, draft_dtype, accepted_len, out_tokens, diag, workspace, workspace_bytes,
                          stream, 1);
     if (rc != SV_OK) return rc;
-    rc = sv_lmhead(hidden, w_packed, M, d, V, target_logits, stream);
-    if (rc != SV_OK) return rc;
+    if (parts & 1) {
+        rc = sv_lmhead(hidden, w_packed, M, d, V, target_logits, stream);
+        if (rc != SV_OK) return rc;
+    }
+    if (!(parts & 2)) return SV_OK;
     return sv_verify_mixed(target_logits, draft_logits, draft_tokens, uniforms, temperature, greedy_flag, B, K,
                            V, SV_F32, draft_dtype, accepted_len, out_tokens, diag, workspace, workspace_bytes,
                            stream, 0);
 }
+
+}  // namespace svlm
+
+extern "C" {
+
+#define SV_LMV_ARGS                                                                                  \
+    const void *hidden, const void *w_packed, int32_t d, float *target_logits, const void *draft_logits, \
+        int32_t draft_dtype, const int32_t *draft_tokens, const float *uniforms, float temperature,     \
+        const uint8_t *greedy_flag, int32_t B, int32_t K, int32_t V, int32_t *accepted_len,              \
+        int32_t *out_tokens, const sv_diag *diag, void *workspace, size_t workspace_bytes, void *stream
+#define SV_LMV_PASS                                                                                  \
+    hidden, w_packed, d, target_logits, draft_logits, draft_dtype, draft_tokens, uniforms, temperature, \
+        greedy_flag, B, K, V, accepted_len, out_tokens, diag, workspace, workspace_bytes, stream
+
+int spec_lmhead_verify(SV_LMV_ARGS) { return svlm::lmhead_verify_parts(3, SV_LMV_PASS); }
+int sv_lmhead_verify_gemm(SV_LMV_ARGS) { return svlm::lmhead_verify_parts(1, SV_LMV_PASS); }
+int sv_lmhead_verify_rest(SV_LMV_ARGS) { return svlm::lmhead_verify_parts(2, SV_LMV_PASS); }
 
 }  // extern "C"

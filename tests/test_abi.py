@@ -136,9 +136,11 @@ def test_lmhead_packed_bytes(lib, d, V, want):
     assert lib.sv_lmhead_packed_bytes(d, V) == want
 
 
-@pytest.mark.parametrize("kw", [dict(draft_dtype=5), dict(T=0.0), dict(K=64), dict(d=12),
-                                dict(ws_bytes=16), dict(uniforms=None)])
-def test_fused_verify_checks_everything_before_launch(lib, kw):
+@pytest.mark.parametrize("kw,want", [
+    (dict(draft_dtype=5), binding.SV_EINVAL), (dict(T=0.0), binding.SV_EINVAL), (dict(K=64), binding.SV_EINVAL),
+    (dict(d=12), binding.SV_EINVAL), (dict(uniforms=None), binding.SV_EINVAL),
+    (dict(ws_bytes=16), binding.SV_EWORKSPACE)])
+def test_fused_verify_checks_everything_before_launch(lib, kw, want):
     a = dict(hidden=FAKE, w=FAKE, d=16, logits=FAKE, draft=FAKE, draft_dtype=1, tokens=FAKE,
              uniforms=FAKE, T=1.0, greedy=None, B=2, K=3, V=100, acc=FAKE, out=FAKE, diag=None,
              ws=FAKE, ws_bytes=binding.workspace_bytes(2, 3, 100, 0))
@@ -146,7 +148,7 @@ def test_fused_verify_checks_everything_before_launch(lib, kw):
     rc = lib.spec_lmhead_verify(a["hidden"], a["w"], a["d"], a["logits"], a["draft"], a["draft_dtype"],
                                 a["tokens"], a["uniforms"], C.c_float(a["T"]), a["greedy"], a["B"], a["K"],
                                 a["V"], a["acc"], a["out"], a["diag"], a["ws"], a["ws_bytes"], None)
-    assert rc in (binding.SV_EINVAL, binding.SV_EWORKSPACE)
+    assert rc == want
 
 
 def test_wait_limit_knob(lib):
