@@ -79,6 +79,8 @@ extern "C" {
 #define SV_ELAUNCH    -3
 #define SV_ESCRATCH   -4
 
+#define SV_GAVE_UP    -2   /* accepted_len of a sequence whose SV_MODE_SEQ wait gave up */
+
 #define SV_MAX_K 63
 #define SV_MAX_NGRAM 64
 
@@ -111,6 +113,8 @@ size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype);
  *   greedy_flag   [B] uint8, 1 = greedy sequence; NULL = all sampling
  * Outputs:
  *   accepted_len  [B] int32: n in [0, K] accepted draft tokens, -1 = invalid
+ *                 input, SV_GAVE_UP (-2) = a SV_MODE_SEQ wait gave up (the
+ *                 row is then unspecified)
  *   out_tokens    [B, K+1] int32: x_0..x_{n-1}, then the correction or bonus
  *                 token, then -1 padding.                                    */
 int spec_verify(const void* target_logits, const void* draft_logits,
@@ -119,6 +123,19 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 int32_t B, int32_t K, int32_t V, int32_t dtype,
                 int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify with the schedule chosen for this call only (SV_MODE_AUTO:
+ * the automatic rule; SV_MODE_EAGER / SV_MODE_LAZY / SV_MODE_SEQ as
+ * sv_set_mode describes), whatever the process-wide mode is: e.g. a caller
+ * that runs other work on the device at the same time asks for
+ * SV_MODE_EAGER, which assumes nothing about which workgroups run together.
+ * SV_EINVAL for another mode value; otherwise as spec_verify.             */
+int spec_verify_mode(int mode, const void* target_logits, const void* draft_logits,
+                     const int32_t* draft_tokens, const float* uniforms,
+                     float temperature, const uint8_t* greedy_flag,
+                     int32_t B, int32_t K, int32_t V, int32_t dtype,
+                     int32_t* accepted_len, int32_t* out_tokens, const sv_diag* diag,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* spec_verify with separate storage types for the target and the draft
  * logits (each SV_F32 or SV_BF16), e.g. fp32 target logits straight from an
@@ -291,8 +308,11 @@ int sv_kv_commit(void* cache, int32_t* cache_len, const void* staged, const int3
  *   final draw in every case; target rows past klen[b] are never read.
  *   klen[b] outside [0, K] marks the sequence invalid (accepted_len -1).
  *   Other arguments, outputs, workspace and errors as spec_verify (no draft
- *   logits; q_tok reports 1 and lse_q 0 for tested positions); always the
- *   eager schedule.                                                       */
+ *   logits; q_tok reports 1 and lse_q 0 for tested positions).  Schedule:
+ *   SV_MODE_SEQ when the mode asks for it or, under SV_MODE_AUTO, when
+ *   position 0's target rows alone are at least 64 MiB (and the vocabulary
+ *   fits that schedule's limit); otherwise eager (SV_MODE_LAZY runs eager:
+ *   the per-position launches take no one-hot rows).                     */
 int sv_lookup_propose(const int32_t* history, const int32_t* hist_len, int32_t B, int32_t Lmax,
                       int32_t n_max, int32_t n_min, int32_t K, int32_t* cand, int32_t* klen, void* stream);
 int spec_verify_lookup(const void* target_logits, int32_t dtype, const int32_t* cand, const int32_t* klen,
@@ -357,19 +377,26 @@ int sv_seq_lookahead(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int3
 
 /* Every wait of the SV_MODE_SEQ exchange is bounded: after this many polls
  * (each one load round trip, about 1 us, so the default bounds a wait
- * at roughly a second) it gives up and the sequence reports accepted_len -1
- * instead of hanging, e.g. when other work keeps some of the call's
- * workgroups from running at the same time: a launch of this schedule
- * assumes the device holds all its workgroups at once, so verify calls in
- * flight together on several streams (or next to other work that fills the
- * device) belong under SV_MODE_EAGER or SV_MODE_LAZY, or in one stream's
- * order.  The default (polls = 0) is
- * 2^20; smaller values are for tests that force the give-up path.  A
- * sampling sequence's accepted_len is written by the workgroup that draws,
- * after the drawn token, so a valid length always stands next to a written
- * token.  Words a give-up leaves in the workspace carry that call's tags and
- * never match a later call, except a replay of the same captured launch.
- * Process-wide; SV_EINVAL for polls outside 0..2^20.                      */
+ * at roughly a second) it gives up and the sequence reports accepted_len
+ * SV_GAVE_UP (-2) instead of hanging, e.g. when other work
+ * keeps some of the call's workgroups from running at the same time: a
+ * launch of this schedule assumes the device holds all its workgroups at
+ * once, so verify calls in flight together on several streams (or next to
+ * other work that fills the device) belong under SV_MODE_EAGER or
+ * SV_MODE_LAZY (spec_verify_mode picks one per call), or in one stream's
+ * order.  -2 is distinct from -1 (invalid input): the inputs may be fine and
+ * the call can be repeated.  Under -2 the row of out_tokens is unspecified
+ * (callers discard it).  A sequence one of whose workgroups gave up while
+ * the others completed holds whichever length was stored last: -2, or the
+ * valid length, which then always stands next to its whole row (the row is
+ * written only by the workgroups that complete, the length last).  The
+ * default (polls = 0) is 2^20; smaller values are for tests that force the
+ * give-up path.  A sampling sequence's valid accepted_len is written by the
+ * workgroup that draws, after the drawn token, so a valid length always
+ * stands next to a written token.  Words a give-up leaves in the workspace
+ * carry that call's tags and never match a later call, except a replay of
+ * the same captured launch.  Process-wide; SV_EINVAL for polls outside
+ * 0..2^20.                                                                */
 int sv_set_wait_limit(int32_t polls);
 
 /* The HIP error code (hipError_t) behind this thread's most recent

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_ELAUNCH, SV_ESCRATCH = 0, -1, -2, -3, -4
+SV_GAVE_UP = -2          # accepted_len of a sequence whose per-sequence wait gave up
 SV_MAX_K = 63
 
 # The exported names, as declared in include/spec_verify.h.
@@ -27,7 +28,7 @@ EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "s
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups", "sv_set_wait_limit",
            "sv_set_seq_lookahead", "sv_seq_lookahead",
            "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
-           "spec_verify_noalloc", "sv_noalloc_scratch_bytes", "sv_strerror", "sv_version")
+           "spec_verify_noalloc", "sv_noalloc_scratch_bytes", "spec_verify_mode", "sv_strerror", "sv_version")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
 
 
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH):
                 fn = getattr(lib, name)
                 fn.restype = C.c_int
                 fn.argtypes = verify_args
+            lib.spec_verify_mode.restype = C.c_int
+            lib.spec_verify_mode.argtypes = [C.c_int] + verify_args
             lib.spec_verify_noalloc.restype = C.c_int
             lib.spec_verify_noalloc.argtypes = verify_args[:13] + [C.c_void_p]
             lib.sv_noalloc_scratch_bytes.restype = C.c_size_t
@@ -225,7 +228,11 @@ def get_workspace(nbytes: int, device, stream=None):
     key = (str(device), int(stream or 0))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        # allocated on the stream that uses it, so the caching allocator hands a
+        # replaced workspace's memory out again only in that stream's order
+        # (the kernels of earlier calls on it may still be reading the old one)
+        with torch.cuda.stream(torch.cuda.ExternalStream(int(stream or 0), device=device)):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 
@@ -259,7 +266,7 @@ class Outputs(dict):
 
 
 def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
-          outputs=None, diag=True, workspace=None, stream=None):
+          outputs=None, diag=True, workspace=None, stream=None, mode=None):
     torch = _torch()
     lib = load_library()
     if target.dim() != 3:
@@ -307,8 +314,15 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
         ws_args = (ws.data_ptr(), ws.numel())
     dts = (dt,) if ddt == dt else (dt, ddt)
     if ddt != dt:
+        if mode is not None:
+            raise TypeError("a per-call schedule needs one storage type for target and draft logits")
         fn_name = "spec_verify_ex"
-    rc = getattr(lib, fn_name)(
+    lead = ()
+    if mode is not None:
+        if fn_name != "spec_verify":
+            raise TypeError("a per-call schedule applies to the whole verify step only")
+        fn_name, lead = "spec_verify_mode", (int(mode),)
+    rc = getattr(lib, fn_name)(*lead,
         target.data_ptr(), None if draft is None else draft.data_ptr(),
         None if tokens is None or tokens.numel() == 0 else tokens.data_ptr(),
         uniforms.data_ptr(), C.c_float(float(temperature)),
@@ -322,7 +336,8 @@ def _call(fn_name, target, draft, tokens, uniforms, temperature, greedy=None, *,
 
 
 def verify(target, draft, tokens, uniforms, temperature, greedy=None, **kw):
-    """spec_verify on torch device tensors -> Outputs(accepted_len, out_tokens[, diagnostics])."""
+    """spec_verify on torch device tensors -> Outputs(accepted_len, out_tokens[, diagnostics]).
+    mode=MODE_* (keyword) picks the schedule for this call only (spec_verify_mode)."""
     return _call("spec_verify", target, draft, tokens, uniforms, temperature, greedy, **kw)
 
 
@@ -755,8 +770,11 @@ def kv_commit(cache, cache_len, staged, accepted_len, offset=1, status=None, str
     _dev_ptr(accepted_len, "accepted_len", torch.int32, (B,))
     if staged is not None:
         _dev_ptr(staged, "staged")
-        if staged.shape[0] != P or staged.shape[1] != B or staged.dtype != cache.dtype or \
-                staged[0, 0, 0].numel() * staged.element_size() != row_bytes:
+        srow = 1
+        for n in staged.shape[3:]:
+            srow *= n
+        if staged.dim() != cache.dim() or staged.shape[0] != P or staged.shape[1] != B or \
+                staged.dtype != cache.dtype or srow * staged.element_size() != row_bytes:
             raise ValueError("staged must be [P, B, K + offset, row] like the cache")
         K = staged.shape[2] - offset
     else:

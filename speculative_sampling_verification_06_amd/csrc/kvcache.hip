@@ -118,12 +118,14 @@ int sv_kv_commit(void* cache, int32_t* cache_len, const void* staged, const int3
     P.row_bytes = row_bytes;
     const int64_t region = (int64_t)P.S * row_bytes;
     const int64_t chunks = (region + svkv::CHUNK - 1) / svkv::CHUNK;
-    if (chunks < 1 || (int64_t)planes * B * chunks > INT_MAX) return SV_EINVAL;
+    // S = K + offset = 0 (K = 0, offset 0): no staged entries, so nothing to
+    // copy; the length update and the status still run
+    if ((int64_t)planes * B * chunks > INT_MAX) return SV_EINVAL;
     P.chunks = (int32_t)chunks;
     P.vec = row_bytes % 16 == 0 && svkv::aligned_to(cache, 16) && (!staged || svkv::aligned_to(staged, 16));
     hipStream_t st = static_cast<hipStream_t>(stream);
     sv_launch_begin();
-    if (staged)
+    if (staged && chunks > 0)
         hipLaunchKernelGGL(svkv::k_kv_copy, dim3((unsigned)((int64_t)planes * B * chunks)), dim3(svkv::NT), 0, st, P);
     hipLaunchKernelGGL(svkv::k_kv_len, dim3((unsigned)((B + svkv::NT - 1) / svkv::NT)), dim3(svkv::NT), 0, st, P,
                        cache_len, status);

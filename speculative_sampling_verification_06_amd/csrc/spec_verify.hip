@@ -1483,6 +1483,17 @@ __device__ __forceinline__ bool gather(const uint64_t* region, int G, uint32_t e
     }
 }
 
+// A member whose bounded wait ran out (some member of its sequence did not run
+// at the same time): the sequence reports SV_GAVE_UP.  It writes the length
+// only: the row is written by the members that complete (member 0 the prefix
+// and padding, the drawing member the final token, then the length), so a
+// valid length, if it is the store that lands last, always stands next to a
+// whole row; under SV_GAVE_UP the row is unspecified (see sv_set_wait_limit).
+__device__ __forceinline__ void give_up(const Params& P, int b)
+{
+    if (threadIdx.x == 0) P.acc[b] = SV_GAVE_UP;
+}
+
 // Draw pass of one member over its slice (segments sg0 .. sg0+nl-1) of row
 // n: per segment, the sum of the draw weights (seg_r: residual max(0, p-q),
 // or p for the bonus row, both scaled by Z_p) and of p (seg_p).  Full
@@ -1748,7 +1759,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         if (sh_stop) break;
     }
     if (sh_stop == 2) {                            // a wait gave up
-        if (tid == 0) P.acc[b] = -1;
+        give_up(P, b);
         return;
     }
 
@@ -1839,8 +1850,8 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
         }
     }
     __syncthreads();
-    if (sh_pick_g == -2) {
-        if (tid == 0) P.acc[b] = -1;
+    if (sh_pick_g == -2) {                         // the wait for the slice totals gave up
+        give_up(P, b);
         return;
     }
     if (sh_pick_g != g) return;                    // another member's slice holds the draw
@@ -2018,9 +2029,12 @@ static int lookahead_for(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t d
 // which pays one latency-bound launch per position (5-20 us each on
 // gfx950), wins once the eager stream is long against K+1 such launches: at
 // least 64 MiB of logits per position; else eager.
-static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd, bool onehot = false)
+// mode: the schedule asked for (SV_MODE_*); SV_MODE_AUTO applies the rule
+// below.  -1: the process-wide mode (sv_set_mode).
+static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t dtd, bool onehot = false,
+                          int mode = -1)
 {
-    const int m = mode_now();
+    const int m = mode >= 0 ? mode : mode_now();
     if (onehot) {                                  // no draft rows; lazy launches do not take one-hot rows
         const double bt = dtt == SV_BF16 ? 2 : 4;
         const bool seq_ok = nseg_of(V) <= QMAXSEG;
@@ -2381,6 +2395,23 @@ size_t sv_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t dtype)
 int spec_verify(SV_ARGS_DECL)
 {
     SV_PREPARE;
+    rc = sv::launch_stats(P, pl, dtype, dtype, st);
+    if (rc != SV_OK) return rc;
+    return sv::launch_draw(P, pl, dtype, dtype, st);
+}
+
+int spec_verify_mode(int mode, SV_ARGS_DECL)
+{
+    if (mode < SV_MODE_AUTO || mode > SV_MODE_SEQ) return SV_EINVAL;
+    if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || !sv::dtype_ok(dtype)) return SV_EINVAL;
+    // SV_MODE_AUTO here means the automatic rule, whatever sv_set_mode says
+    const int force = sv::choose_sched(B, K, V, dtype, dtype, false, mode);
+    sv::Params P;
+    sv::Plan pl;
+    int rc = sv::prepare(target_logits, draft_logits, draft_tokens, uniforms, temperature, greedy_flag, B, K, V,
+                         dtype, dtype, accepted_len, out_tokens, diag, workspace, workspace_bytes, &P, &pl, force);
+    if (rc <= 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
     rc = sv::launch_stats(P, pl, dtype, dtype, st);
     if (rc != SV_OK) return rc;
     return sv::launch_draw(P, pl, dtype, dtype, st);

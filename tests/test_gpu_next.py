@@ -159,3 +159,19 @@ def test_verify_then_commit_over_rounds(dev):
             rows = got[0, b, :len(stream[b])].view(np.int64).reshape(-1, 2)
             assert rows[:, 0].tolist() == [int(t) for t in stream[b]]
             assert rows[:, 1].tolist() == list(range(len(stream[b])))
+
+
+def test_kv_commit_without_entries(dev):
+    """K = 0 with offset 0: no staged entries (S = 0).  Nothing is copied; each
+    length stays (c_b = 0) with status 0, invalid sequences get status 1."""
+    import torch
+    P, B, L, row = 2, 5, 16, 64
+    cache = torch.zeros(P, B, L, row, dtype=torch.uint8, device=dev)
+    ln = torch.tensor([0, 3, 7, 16, 2], dtype=torch.int32, device=dev)
+    acc = torch.tensor([0, 0, -1, 0, 0], dtype=torch.int32, device=dev)
+    staged = torch.empty(P, B, 0, row, dtype=torch.uint8, device=dev)
+    st = binding.kv_commit(cache, ln, staged, acc, 0)
+    torch.cuda.synchronize()
+    assert ln.cpu().tolist() == [0, 3, 7, 16, 2]
+    assert st.cpu().tolist() == [0, 0, 1, 0, 0]
+    assert int(cache.sum()) == 0

@@ -356,9 +356,10 @@ def test_seq_wait_give_up_marks_invalid_then_recovers(dev, la):
         binding.set_wait_limit(1)
         _log("[giveup] one poll per wait")
         g = run_gpu(w, dev, workspace=ws)
-        bad = g["accepted_len"] == -1
+        bad = g["accepted_len"] == binding.SV_GAVE_UP
         _log(f"[giveup] {int(bad.sum())} of {w.B} sequences gave up")
         assert bad.any()
+        assert not np.any(g["accepted_len"] == -1)     # valid inputs: never reported as invalid
         ok = np.where(~bad)[0]
         if len(ok):
             ws_ = _subset(w, ok)
@@ -436,3 +437,29 @@ def test_seq_beyond_lds_vocab_uses_lazy(dev):
         check(w, dev)
     finally:
         binding.set_mode(binding.MODE_AUTO)
+
+
+def test_per_call_mode_overrides_process_mode(dev):
+    """spec_verify_mode: the process-wide mode is the per-sequence schedule with
+    every wait bounded to one poll (sequences give up there); a call that asks
+    for the eager schedule runs it and agrees with the oracle everywhere, a call
+    that asks for the per-sequence one gives up again, and AUTO applies the
+    automatic rule (eager at this size)."""
+    mask = (np.arange(64) % 5 == 2).astype(np.uint8)
+    w = I.synth_logits(4243, 64, 6, 20000, dtype=I.BF16, T=0.9, sigma=3.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=0.4, greedy_mask=mask, name="per_call_mode")
+    o = oracle.verify(w)
+    binding.set_mode(binding.MODE_SEQ)
+    binding.set_wait_limit(1)
+    try:
+        for m in (binding.MODE_EAGER, binding.MODE_LAZY):
+            g = run_gpu(w, dev, mode=m)
+            _log(f"[mode] per-call {m}: {parity.compare(w, g, o)}")
+        g = run_gpu(w, dev, mode=binding.MODE_SEQ)
+        assert np.any(g["accepted_len"] == binding.SV_GAVE_UP)
+        _log(f"[mode] per-call seq: {int(np.sum(g['accepted_len'] == binding.SV_GAVE_UP))} gave up")
+    finally:
+        binding.set_wait_limit(0)
+        binding.set_mode(binding.MODE_AUTO)
+    g = run_gpu(w, dev, mode=binding.MODE_AUTO)
+    parity.compare(w, g, o)
