@@ -352,7 +352,10 @@ int sv_schedule(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t d
 /* Under SV_MODE_SEQ each sequence gets G workgroups that split every row it
  * reaches and exchange partial statistics through the workspace (tagged
  * words; nothing to initialise), G as large as the device holds all of them
- * at once; G = 1 is one 1024-thread workgroup per sequence.
+ * at once; with lookahead (below) G stops at the fewest workgroups that
+ * cover a row in one pass of their loads (1 KiB x 16 per workgroup for
+ * bf16 rows, x 8 when a row is fp32), since every further workgroup only
+ * lengthens the exchange; G = 1 is one 1024-thread workgroup per sequence.
  * sv_set_seq_groups caps G (1..64; 0 = no cap, the default; the environment
  * variable SV_SEQ_GROUPS sets the initial cap); SV_EINVAL otherwise.
  * sv_seq_groups: the G a call of this shape would use now (0 when it would
@@ -365,10 +368,11 @@ int sv_seq_groups(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int32_t
  * position j, which hides the exchange's round trip behind a stream at the
  * price of one position read past the first rejection (never used; rows past
  * the rejection still never change the result); with 0 they stream a
- * position only once the previous one is settled.  sv_set_seq_lookahead:
+ * position only once the previous one is settled; with 2 they run two
+ * positions ahead (two rows read past the rejection).  sv_set_seq_lookahead:
  * -1 = by shape (the default: 1 while position 0 alone streams less than
- * 64 MiB, else 0; the environment variable SV_SEQ_LOOKAHEAD=0|1 sets an
- * initial override), 0 or 1 to force it; SV_EINVAL otherwise.
+ * 64 MiB, else 0; the environment variable SV_SEQ_LOOKAHEAD=0|1|2 sets an
+ * initial override), 0, 1 or 2 to force it; SV_EINVAL otherwise.
  * sv_seq_lookahead: the lookahead a call of this shape would use now (0 when
  * it would not run SV_MODE_SEQ with several workgroups per sequence),
  * SV_EINVAL for a shape the call would reject.                            */

@@ -334,6 +334,30 @@ def _subset(w, idx):
                       w.uniforms[idx], w.greedy[idx])
 
 
+def test_seq_members_under_lookahead(dev):
+    """With lookahead a sequence gets the fewest workgroups whose slices one
+    pass of their loads covers (16 one-KiB segments of a bf16 row, 8 with an
+    fp32 row), never more than the device holds at once; without lookahead
+    (forced off) it gets as many as the device holds."""
+    bf, f32 = binding.SV_BF16, binding.SV_F32
+    binding.set_mode(binding.MODE_SEQ)
+    binding.set_seq_groups(0)
+    try:
+        for (B, K, V, dt), want in (((32, 8, 152064, bf), 19), ((64, 5, 128256, bf), 16),
+                                   ((32, 5, 64000, f32), 16)):
+            binding.set_seq_lookahead(-1)
+            assert binding.seq_lookahead(B, K, V, dt) >= 1
+            g = binding.seq_groups(B, K, V, dt)
+            _log(f"[members] B={B} K={K} V={V} dtype={dt}: G={g} with lookahead")
+            assert 2 <= g <= want
+            binding.set_seq_lookahead(0)
+            g0 = binding.seq_groups(B, K, V, dt)
+            assert g0 >= g
+    finally:
+        binding.set_mode(binding.MODE_AUTO)
+        binding.set_seq_lookahead(-1)
+
+
 @pytest.mark.parametrize("la", [0, 1], ids=["seq", "seqla"])
 def test_seq_wait_give_up_marks_invalid_then_recovers(dev, la):
     """Every wait of the per-sequence exchange bounded to one poll from the host
