@@ -114,6 +114,43 @@ def test_fused_lmhead_verify_full_size(dev, mode, groups, la):
         binding.set_seq_lookahead(-1)
 
 
+@pytest.mark.parametrize("B,K,d,V", [(40, 4, 256, 1000), (7, 3, 72, 515), (3, 0, 64, 300)])
+def test_lmhead_verify_greedy_ragged_invalid(dev, B, K, d, V):
+    """Every other sequence greedy (its first proposals the target's argmax, so
+    some are accepted), V not a multiple of 256 (a partial last column block),
+    B*(K+1) above 192 (two row blocks) or not a multiple of 32, and two
+    sequences with NaN hidden states at position 0 (invalid).  The oracle runs
+    on the GPU's own fp32 logits, so greedy decisions must agree exactly."""
+    import torch
+    w = I.cfg_lmhead(seed=77 + B + V, B=B, K=K, d=d, V=V, draft_noise=0.3)
+    w.greedy = (np.arange(B) % 2 == 0).astype(np.uint8)
+    tgt64 = oracle.lmhead_logits(w.hidden, w.w_lm)
+    tokens = w.tokens.copy()
+    for b in range(0, B, 2):
+        for j in range(min(K, b % (K + 2))):
+            tokens[b, j] = int(np.argmax(tgt64[b, j]))
+    w.tokens = tokens
+    hidden = w.hidden.copy()
+    if B >= 4:
+        hidden[2, 0, d // 2] = 0x7FC0          # bf16 NaN: row 0 of a greedy sequence
+        hidden[3, 0, 1] = 0x7FC0               # and of a sampling sequence
+    w.hidden = hidden
+    _log(f"[lmhead] greedy/ragged B={B} K={K} d={d} V={V}")
+    d_h = binding.bf16_tensor(w.hidden, dev)
+    wt = binding.lmhead_pack(binding.bf16_tensor(w.w_lm, dev))
+    dd = binding.to_device(w, dev)
+    out = binding.lmhead_verify(d_h, wt, dd["draft"], dd["tokens"], dd["uniforms"], w.T, dd["greedy"])
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    o = oracle.verify(w, target=g["target_logits"].astype(np.float64))
+    rep = parity.compare(w, g, o)
+    _log(f"[lmhead] parity {rep}; lengths {o.accepted_len.tolist()}")
+    if B >= 4:
+        assert g["accepted_len"][2] == -1 and g["accepted_len"][3] == -1
+    assert (g["accepted_len"][0::2] > 0).any() or K == 0      # some greedy proposals accepted
+    assert rep["flagged_mismatch"] == []
+
+
 def _fused_case(dev):
     import torch
     w = I.cfg_lmhead()
