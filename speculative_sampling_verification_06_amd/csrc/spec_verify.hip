@@ -2051,9 +2051,10 @@ static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t 
     const double p0 = pos0_bytes(B, K, V, dtt, dtd);
     if (seq_ok && p0 >= mib64) return SEQ;
     // a few long bf16 rows per sequence: the per-sequence schedule with
-    // lookahead (measured: B=64 K=5 V=128256 35 against 41 us eager, B=32
-    // K=8 V=152064 38 against 47 us); not at B=256 over a 19008-token shard
-    // (54 against 46 us) nor for fp32 target rows (57 against 42 us)
+    // lookahead (measured per step with the caches warm: B=64 K=5 V=128256
+    // 35.5 against 41 us eager, B=32 K=8 V=152064 28.6 against 47 us); not
+    // at B=256 over a 19008-token shard (45.7 against 45.8 us) nor for fp32
+    // target rows (50 against 42-44 us)
     if (seq_ok && K > 0 && p0 >= mib64 / 4 && B <= 64 && dtt == SV_BF16) return SEQ;
     if (K == 0) return EAGER;
     const double bytes = (double)B * V * ((double)(K + 1) * bt + (double)K * bd);
