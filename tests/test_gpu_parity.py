@@ -7,6 +7,7 @@ chunk and segment tails, K = 0 and K = 63, invalid inputs, determinism, the
 split launches and a 10^6-trial chi-square of the GPU's own output law.
 """
 
+import copy
 import os
 import sys
 
@@ -332,6 +333,48 @@ def _subset(w, idx):
     dr = None if w.draft is None else w.draft[idx]
     return I.Workload(w.name + "_sub", len(idx), w.K, w.V, w.dtype, w.T, w.target[idx], dr, w.tokens[idx],
                       w.uniforms[idx], w.greedy[idx])
+
+
+@SCHED
+def test_graph_replays_match_eager_calls(dev, schedule):
+    """The verify step captured in a HIP graph (torch.cuda.CUDAGraph on a side
+    stream) and replayed four times, the uniforms rewritten before each replay
+    and an eager call on the same inputs in between: every replay equals that
+    eager call bit for bit and agrees with the oracle.  Under the per-sequence
+    schedule the replays reuse the captured call's host nonce, so only the
+    device-side call counter in the exchange tags tells them apart."""
+    import torch
+    mask = (np.arange(24) % 3 == 1).astype(np.uint8)
+    w = I.synth_logits(9100, 24, 5, 20000, dtype=I.BF16, T=0.8, sigma=3.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=0.4, greedy_mask=mask, name="graph")
+    d = binding.to_device(w, dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call = binding.Bound(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], d["greedy"],
+                             stream=side.cuda_stream)
+        for _ in range(3):
+            call.verify()
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call.verify()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    for rep in range(4):
+        u = I.grid_uniforms(rng, (w.B, w.K + 1)) if rep else w.uniforms
+        d["uniforms"].copy_(torch.from_numpy(np.ascontiguousarray(u, np.float32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in call.outputs.items()}
+        wr = copy.copy(w)
+        wr.uniforms = np.asarray(u, np.float32)
+        ref = run_gpu(wr, dev)                     # eager work between the replays
+        for k in ("accepted_len", "out_tokens", "p_tok", "lse_p", "res_mass"):
+            assert np.array_equal(got[k], ref[k], equal_nan=True), (rep, k)
+        rep_o = parity.compare(wr, got, oracle.verify(wr))
+        _log(f"[graph] replay {rep}: {rep_o}")
 
 
 def test_seq_members_under_lookahead(dev):
