@@ -747,13 +747,26 @@ __device__ void decide_core(const Params& P, int b, bool greedy, bool write_out,
 }
 
 // Merges the sequence's chunk partials into row statistics, then decides.
+// The last wave loads the tests' inputs (tokens, uniforms, the two logits at
+// each token) while the rows merge, so the decision waits for one round trip
+// instead of two after the merge.
 template <int DTT, int DTD>
 __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, Decision* dec)
 {
     const int K = P.K, C = P.C, R = 2 * K + 1;
     const int tid = threadIdx.x;
     __shared__ RowStat f_rs[MAXR];
+    __shared__ TestIn ti[SV_MAX_K + 1];
 
+    const int tw = (NWAVE - 1) * 64;               // R <= 127 rows merge on the waves before it
+    if (tid >= tw && tid - tw <= K) {
+        const int j = tid - tw;
+        // prompt lookup: positions at or past the sequence's own count are
+        // never tested (their proposals and rows stay unread)
+        const int kb = P.klen ? P.klen[b] : K;
+        const bool tested = j == K || (kb >= 0 && kb <= K && j < kb);
+        ti[j] = tested ? load_test_in<DTT, DTD>(P, b, j, greedy) : TestIn{-1, 0.f, 0.f, 0.f};
+    }
     if (tid < R) {
         const Partial* pp = P.part + ((int64_t)b * R + tid) * C;
         const bool draft_row_ = tid > K;
@@ -762,8 +775,8 @@ __device__ void decide_seq(const Params& P, int b, bool greedy, bool write_out, 
         else f_rs[tid] = merge_row(pp, C, P.s, greedy);
     }
     __syncthreads();
-    if (P.klen) decide_core<DTT, DTD, true>(P, b, greedy, write_out, false, f_rs, nullptr, dec);
-    else decide_core<DTT, DTD, false>(P, b, greedy, write_out, false, f_rs, nullptr, dec);
+    if (P.klen) decide_core<DTT, DTD, true>(P, b, greedy, write_out, false, f_rs, ti, dec);
+    else decide_core<DTT, DTD, false>(P, b, greedy, write_out, false, f_rs, ti, dec);
 }
 
 // --------------------------- k_rowstats_lazy: position j, live rows only --
