@@ -1015,16 +1015,19 @@ __device__ Locate locate_segment(const float* sums, int nseg, float thr, float* 
 }
 
 // Total weight of the segment sums: residual sums_r, or p sums sums_p when
-// the residual rounded to nothing; then the segment holding u*S.
+// the residual rounded to nothing; then the segment holding u*S.  first_r:
+// this thread's entry of the first BT residual sums when the caller already
+// loaded it (NAN: not loaded).
 template <int BT>
 __device__ Pick find_segment(const float* sums_r, const float* sums_p, int nseg, float u, bool bonus,
-                             float* sh_scan, int* sh_seg, float* sh_lo)
+                             float* sh_scan, int* sh_seg, float* sh_lo, float first_r = NAN)
 {
     const int tid = threadIdx.x;
     Pick pk;
     float S = 0.f;
     for (int base = 0; base < nseg; base += BT) {
-        const float v = (base + tid < nseg) ? sums_r[base + tid] : 0.f;
+        const float v = (base == 0 && !(first_r != first_r)) ? first_r
+                                                            : ((base + tid < nseg) ? sums_r[base + tid] : 0.f);
         float tot;
         block_incl_scan<BT>(v, sh_scan, &tot);
         S += tot;
@@ -1108,9 +1111,14 @@ template <int DTT, int DTD>
 __global__ __launch_bounds__(NT) void k_search(const Params P)
 {
     const int b = blockIdx.x;
+    const int nseg = P.nseg;
+    // the first residual sums load with the record (the search needs them
+    // whenever the record says there is a draw)
+    const float* sums_r = P.seg + (int64_t)b * nseg;
+    const float first_r = (int)threadIdx.x < nseg ? sums_r[threadIdx.x] : 0.f;
     const SeqRec rec = P.rec[b];
     if (rec.status != 1) return;
-    const int K = P.K, nseg = P.nseg;
+    const int K = P.K;
     const float s = P.s;
     const int n = rec.n;
     const bool bonus = rec.bonus != 0;
@@ -1124,9 +1132,8 @@ __global__ __launch_bounds__(NT) void k_search(const Params P)
     __shared__ int sh_seg[NWAVE];
     __shared__ float sh_lo[1];
 
-    const float* sums_r = P.seg + (int64_t)b * nseg;
     const float* sums_p = P.seg + ((int64_t)P.B + b) * nseg;
-    const Pick pk = find_segment<NT>(sums_r, sums_p, nseg, rec.u, bonus, sh_scan, sh_seg, sh_lo);
+    const Pick pk = find_segment<NT>(sums_r, sums_p, nseg, rec.u, bonus, sh_scan, sh_seg, sh_lo, first_r);
     if ((threadIdx.x >> 6) == 0 && pk.g >= 0) {
         const int y = walk_segment<DTT, DTD>(trow, drow, P.V, pk, s, cp, cq, w, (oh && !bonus) ? rec.xn : -1);
         if (threadIdx.x == 0) {
