@@ -227,9 +227,28 @@ __device__ __forceinline__ AmState am_merge(AmState a, AmState b)
     return r;
 }
 
-template <int N>
+// Online softmax over one window of N elements: the running max m and the
+// sum z of exp2((x - m) s), rescaled when the max moves.  KEEP: once every
+// lane of the wave holds a finite m, a window's exps are taken against m as
+// it stands and added (fp32 sums are scale-invariant, so this is as exact as
+// rescaling, and it spares the window max and the rescale exp; m is then a
+// reference at or below the max); a window whose sum is not below 2^64 on
+// some lane (an element far above m, +Inf or NaN) takes the max and
+// rescales.  KEEP costs registers (the window stays live through its exps).
+template <int N, bool KEEP = false>
 __device__ __forceinline__ void sm_window(const float* x, float s, SmState& st)
 {
+    if (KEEP && __all(st.m > NEG_INF && st.m < POS_INF)) {
+        const float c = st.m * s;
+        float t[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) t[k] = ex2(__builtin_fmaf(x[k], s, -c));
+        const float ws = tree_sum<N>(t);
+        if (__all(ws < 0x1p64f)) {
+            st.z += ws;
+            return;
+        }
+    }
     const float wm = tree_max<N>(x);
     const float mn = vmax(st.m, wm);
     const float cn = shift_of(mn, s);
@@ -260,7 +279,7 @@ __device__ __forceinline__ void am_window(const float* x, IdxF idx, AmState& st)
 
 // Stream elements [e0, e1) of one row (e0 a multiple of E) into the state;
 // BT threads, U 16-byte loads in flight per lane.
-template <int DT, bool GREEDY, int BT = NT, int U = UNROLL>
+template <int DT, bool GREEDY, int BT = NT, int U = UNROLL, bool KEEP = false>
 __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t e1, float s,
                                            SmState& sm, AmState& am)
 {
@@ -286,14 +305,14 @@ __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t 
             if constexpr (GREEDY)
                 am_window<W>(x, [base](int k) { return (base + (int64_t)(k / E) * BT) * E + (k % E); }, am);
             else
-                sm_window<W>(x, s, sm);
+                sm_window<W, KEEP>(x, s, sm);
         }
         const int64_t t0 = v1 * E;             // ragged tail of the row (< E elements)
         if (t0 + tid < e1) {
             float x1[1] = {load1<DT>(row, t0 + tid)};
             const int64_t i1 = t0 + tid;
             if constexpr (GREEDY) am_window<1>(x1, [i1](int) { return i1; }, am);
-            else sm_window<1>(x1, s, sm);
+            else sm_window<1, KEEP>(x1, s, sm);
         }
     } else {
         for (int64_t base = e0 + tid; base < e1; base += (int64_t)BT * W) {
@@ -306,7 +325,7 @@ __device__ __forceinline__ void scan_chunk(const char* row, int64_t e0, int64_t 
             if constexpr (GREEDY)
                 am_window<W>(x, [base](int k) { return base + (int64_t)k * BT; }, am);
             else
-                sm_window<W>(x, s, sm);
+                sm_window<W, KEEP>(x, s, sm);
         }
     }
 }
@@ -471,7 +490,7 @@ __device__ __forceinline__ void rowstats_body(const Params& P, const char* row, 
         am = block_reduce_am(am, sh_am);
         if (threadIdx.x == 0) *dst = {am.v, 0.f, am.i, am.bad};
     } else {
-        if (e0 < e1) scan_chunk<DT, false>(row, e0, e1, P.s, sm, am);
+        if (e0 < e1) scan_chunk<DT, false, NT, UNROLL, true>(row, e0, e1, P.s, sm, am);
         sm = block_reduce_sm(sm, P.s, sh_sm);
         if (threadIdx.x == 0) *dst = {sm.m, sm.z, 0, 0u};
     }
