@@ -300,6 +300,39 @@ def test_schedules_ragged(dev, schedule, B, K, V, dtype, greedy_every, sd):
 
 
 @SCHED
+@pytest.mark.parametrize("dtype", [I.BF16, I.F32], ids=["bf16", "f32"])
+def test_schedules_late_spikes(dev, schedule, dtype):
+    """Rows whose largest logits sit late and far above everything before
+    them (at T = 0.25 a spike of 40 is ~200 in exp2 units over the rest): a
+    running reference taken from early elements must move up, not overflow.
+    Spikes in target and draft rows at several offsets, two rising spikes in
+    some rows, and a late NaN / +Inf (invalid sequences)."""
+    B, K, V = 10, 3, 50000
+    w = I.synth_logits(4242, B, K, V, dtype=I.F32, T=0.25, sigma=1.0, zipf=False, draft_scale=1.0,
+                       draft_sigma=0.5, greedy_mask=(np.arange(B) % 4 == 3).astype(np.uint8), name="late_spikes")
+    t, d = w.target.copy(), w.draft.copy()
+    rng = np.random.default_rng(4243)
+    for b in range(B):
+        for j in range(K + 1):
+            pos = int(rng.integers(V // 2, V))
+            t[b, j, pos] = 40.0 + float(rng.integers(0, 8))
+            if b % 2 == 0:                       # a second, higher spike later still
+                t[b, j, min(V - 1, pos + 777)] = 60.0
+            if j < K:
+                d[b, j, int(rng.integers(V // 3, V))] = 35.0
+    t[5, 0, V - 3] = np.nan                  # examined row: invalid
+    d[6, 0, V - 9] = np.inf                  # examined draft row: invalid
+    tok = w.tokens.copy()
+    tok[1, 0] = int(np.argmax(t[1, 0]))      # a proposal at the spike: accepted
+    if dtype == I.BF16:
+        t, d = I.f32_to_bf16_bits(t), I.f32_to_bf16_bits(d)
+    w2 = I.Workload(f"late_spikes_{I.DTYPE_NAMES[dtype]}", B, K, V, dtype, w.T, t, d, tok, w.uniforms, w.greedy)
+    g, o, rep = check(w2, dev)
+    assert rep["invalid"] >= 2
+    assert g["accepted_len"][1] >= 1
+
+
+@SCHED
 def test_schedules_invalid_inputs(dev, schedule):
     test_masked_tokens_and_invalid_inputs(dev)
 
