@@ -112,6 +112,8 @@ struct Params {
     int32_t B, K, V, C;
     int32_t nseg, tiles;
     int32_t G, gsegs; // grouped schedule: workgroups per sequence, segments per workgroup slice
+    int32_t qd, ncu;  // grouped schedule with lookahead: sequence slots and compute units per die
+                      // for the turned placement (ncu 0: the plain one)
     uint32_t salt;    // grouped schedule: shape hash folded into the tags
     uint32_t nonce;   // grouped schedule: per-call host counter folded into the tags
     int32_t spin;     // grouped schedule: polls before a wait gives up
@@ -1636,14 +1638,27 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
 {
     const int G = P.G;
     const int xcd = (int)(blockIdx.x % XCDS), loc = (int)(blockIdx.x / XCDS);
-    const int q = loc / G;
-    // members of a sequence share a die.  With lookahead (few sequences, 8 or
-    // fewer per die) slot q of die x holds sequence 8q + (x + q) mod 8, so a
-    // pattern over the sequence index with period 2, 4 or 8 (e.g. every other
-    // sequence greedy) is spread over all dies instead of loading some dies
-    // with all the draft rows and draws.  Otherwise slot q holds 8q + x.
+    // members of a sequence share a die (workgroup i runs on die i % 8):
+    // slot q of die x holds sequence 8q + x, members in consecutive slots;
+    // under lookahead 8q + (x + q) mod 8, so a pattern over the sequence
+    // index with period 2, 4 or 8 (e.g. every other sequence greedy) is
+    // spread over all dies
+    int slot = loc;
+    if (LA > 0 && P.ncu > 0) {
+        // a die fills its ncu compute units in turn (its workgroup `loc` on
+        // unit loc % ncu, round loc / ncu); every full round after the first
+        // is turned by half the units, so the slots that share a unit come
+        // from different halves of the rounds' sequences (with the pattern
+        // above: sampling and greedy members side by side, instead of units
+        // that hold only sampling members' rows, exps and draws).  A
+        // rotation within each round keeps every sequence's members in the
+        // rounds they had: a bijection, the same dispatch order.
+        const int ncu = P.ncu, r = loc / ncu, c = loc - r * ncu;
+        if (r < P.qd * G / ncu) slot = r * ncu + (c + ncu - (r * (ncu / 2)) % ncu) % ncu;
+    }
+    const int q = slot / G;
     const int b = LA > 0 ? XCDS * q + (xcd + q) % XCDS : xcd + XCDS * q;
-    const int g = loc - q * G;
+    const int g = slot - q * G;
     if (b >= P.B) return;
     const int K = P.K, V = P.V, R = 2 * K + 1;
     const float s = P.s;
@@ -2032,6 +2047,18 @@ static int group_capacity_t()
     return cus * per_cu;
 }
 
+// Compute units per accelerator die of the current device (0 if unknown).
+static int cus_per_die()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return cus % XCDS == 0 ? cus / XCDS : 0;
+}
+
 static int group_capacity(int32_t dtt, int32_t dtd, bool onehot)
 {
     if (onehot) return dtt == SV_BF16 ? group_capacity_t<SV_BF16, SV_BF16, true>()
@@ -2209,6 +2236,8 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
     P->slots = reinterpret_cast<uint64_t*>(w + pl->off_slots);
     P->G = 1;
     P->gsegs = pl->nseg;
+    P->qd = 0;
+    P->ncu = 0;
     P->salt = 0;
     P->nonce = 0;
     P->spin = GSPIN;
@@ -2244,6 +2273,12 @@ static int prepare(const void* target, const void* draft, const int32_t* tokens,
             for (uint32_t x : f) h = (h ^ x) * 0x01000193u;
             P->G = pl->G;
             P->gsegs = pl->gsegs;
+            // turned placement under lookahead (sequence slots per die, units per die)
+            const int ncu = la > 0 ? cus_per_die() : 0;
+            if (ncu >= 2) {
+                P->qd = (B + XCDS - 1) / XCDS;
+                P->ncu = ncu;
+            }
             P->salt = h;
             P->nonce = g_nonce.fetch_add(1u, std::memory_order_relaxed);
             P->spin = g_spin.load(std::memory_order_relaxed);
