@@ -122,6 +122,7 @@ constexpr int A_PER_T = A_PIECES / NT; // per thread (6)
 constexpr int RB = 2;                  // weight ring depth in LDS blocks
 constexpr int WPF = RB * KS;           // weight prefetch depth in k-steps
 static_assert(A_PIECES % NT == 0, "block pieces must split evenly");
+static_assert(RB % 2 == 0, "block groups must start on an even block (hidden-state register sets alternate)");
 
 __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wp,
                                                   float* __restrict__ out, int M, int d, int V)
@@ -158,22 +159,28 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
     for (int i = 0; i < A_PER_T; ++i) hs[i] = H + (int64_t)min(m0 + ar + RP * i, M - 1) * d + ac;
     // columns past d are stored as zero (the weight's are zero there too,
     // and a finite 0 * 0 keeps a non-finite hidden value elsewhere out); the
-    // select sits at the store, which waits for the loads anyway
-    uint4 sa[A_PER_T];
-    uint32_t amask;                     // all ones while the loaded columns are below d
-#define LM_LOAD_A(kb)                                                                          \
+    // select sits at the store, which waits for the loads anyway.  Two
+    // register sets: a block is loaded two blocks (2*KS k-steps) before its
+    // store, so the store's wait, which also covers every weight fragment
+    // issued before those loads (the counter completes in issue order), asks
+    // only for fragments whose k-step has come: the weight ring keeps its
+    // full lead at block boundaries (one block ahead it fell to half, ~18 us
+    // of the 104 us main loop at B*(K+1) = 192, d = 4096, V = 128256).
+    uint4 sa[2][A_PER_T];
+    uint32_t amask[2];                  // all ones while the loaded columns are below d
+#define LM_LOAD_A(kb, set)                                                                     \
     do {                                                                                       \
         const bool ok_ = (kb) < nblk && (kb) * BK + ac < d;                                   \
-        amask = ok_ ? ~0u : 0u;                                                               \
+        amask[set] = ok_ ? ~0u : 0u;                                                          \
         const int64_t o_ = ok_ ? (int64_t)(kb) * BK : 0;                                      \
         _Pragma("unroll") for (int i_ = 0; i_ < A_PER_T; ++i_)                               \
-            sa[i_] = *reinterpret_cast<const uint4*>(hs[i_] + o_);                            \
+            sa[set][i_] = *reinterpret_cast<const uint4*>(hs[i_] + o_);                       \
     } while (0)
-#define LM_STORE_A(buf)                                                                        \
+#define LM_STORE_A(buf, set)                                                                   \
     do {                                                                                       \
         uint16_t* a_ = &As[buf][ar * A_LD + ac];                                              \
         _Pragma("unroll") for (int i_ = 0; i_ < A_PER_T; ++i_)                               \
-            *reinterpret_cast<uint4*>(a_ + i_ * RP * A_LD) = and4(sa[i_], amask);             \
+            *reinterpret_cast<uint4*>(a_ + i_ * RP * A_LD) = and4(sa[set][i_], amask[set]);   \
     } while (0)
 
     f32x16 acc[MT][NC];
@@ -186,9 +193,10 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
     for (int q = 0; q < WPF; ++q)
 #pragma unroll
         for (int c = 0; c < NC; ++c) wb[q][c] = ldw(c, q);
-    LM_LOAD_A(0);
-    LM_STORE_A(0);
-    LM_LOAD_A(1);
+    LM_LOAD_A(0, 0);
+    LM_STORE_A(0, 0);
+    LM_LOAD_A(1, 1);
+    LM_LOAD_A(2, 0);
     __syncthreads();
 
     // blocks in groups of RB so every weight ring slot index is a compile-time
@@ -228,11 +236,13 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
                                 acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][t], bc[c], acc[t][c], 0, 0, 0);
                     }
                 }
-                // block kb+1 (in registers) into the other buffer; every wave
-                // finished reading that buffer before the previous barrier
-                LM_STORE_A(buf ^ 1);
+                // block kb+1 (register set (kb+1) & 1 = (h+1) & 1, kb0 being
+                // even) into the other buffer; every wave finished reading that
+                // buffer before the previous barrier; then block kb+3 into the
+                // freed set
+                LM_STORE_A(buf ^ 1, (h + 1) & 1);
                 lds_barrier();
-                LM_LOAD_A(kb + 2);
+                LM_LOAD_A(kb + 3, (h + 1) & 1);
             }
         }
     }
