@@ -2118,7 +2118,7 @@ static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t 
     if (seq_ok && p0 >= mib64) return SEQ;
     // a few long bf16 rows per sequence: the per-sequence schedule with
     // lookahead (measured per step with the caches warm: B=64 K=5 V=128256
-    // 35.5 against 41 us eager, B=32 K=8 V=152064 28.6 against 47 us); not
+    // 33.7 against 41 us eager, B=32 K=8 V=152064 29.0 against 47 us); not
     // at B=256 over a 19008-token shard (45.7 against 45.8 us) nor for fp32
     // target rows (50 against 42-44 us)
     if (seq_ok && K > 0 && p0 >= mib64 / 4 && B <= 64 && dtt == SV_BF16) return SEQ;
