@@ -2047,16 +2047,25 @@ static int group_capacity_t()
     return cus * per_cu;
 }
 
-// Compute units per accelerator die of the current device (0 if unknown).
+// Compute units per accelerator die of the current device, cached per
+// device (0 if unknown: the plain placement is used).
 static int cus_per_die()
 {
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
         return 0;
     }
-    return cus % XCDS == 0 ? cus / XCDS : 0;
+    static std::atomic<int> cache[64];
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int per = cus % XCDS == 0 ? cus / XCDS : 0;
+    if (per > 0) cache[dev].store(per, std::memory_order_relaxed);
+    return per;
 }
 
 static int group_capacity(int32_t dtt, int32_t dtd, bool onehot)
