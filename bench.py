@@ -361,7 +361,9 @@ def bench_sample(args, torch, np, binding, I, dev):
         call()
     ms, ev = _timed_one(torch, stream, args.steps, call)
     tok = call().cpu().numpy()
-    bytes_ = w.B * w.V * 2 + w.B * w.V * 2            # every row once, then the drawn row once more
+    # every row once (the bonus-row stream keeps its segment sums, so the draw
+    # reads only the one segment it walks)
+    bytes_ = w.B * w.V * 2 + w.B * 512 * 2
     res = _base_result(w, args.steps, args.warmup, ms, "f32")
     res["metric"] = "draft-step sampled logits/s (B·V per sec), 1 GPU"
     res["value"] = w.B * w.V / (ms * 1e-3)

@@ -431,6 +431,18 @@ __device__ __forceinline__ float wave_sum(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Largest value over the wave (NaN-propagating), the same butterfly as wave_sum.
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = vmax(v, dpp<0xb1>(v, NEG_INF));
+    v = vmax(v, dpp<0x4e>(v, NEG_INF));
+    v = vmax(v, dpp<0x141>(v, NEG_INF));
+    v = vmax(v, dpp<0x140>(v, NEG_INF));
+    v = vmax(v, dpp<0x142, 0xa>(v, NEG_INF));
+    v = vmax(v, dpp<0x143, 0xc>(v, NEG_INF));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Inclusive scan over the wave (lane order): within each row of 16 lanes by
 // shifts of 1, 2, 4 and 8, then the rows' totals carried forward.
 __device__ __forceinline__ float wave_incl_scan(float v)
@@ -1625,6 +1637,57 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     }
 }
 
+// The bonus row's slice of a sampling sequence in one pass (bf16 rows,
+// 16-byte aligned, whole vectors): load u of iteration it of wave w covers
+// exactly segment (it*U + u)*(BT/64) + w of the slice (64 lanes x 8
+// elements), so each segment's max and its sum of exp2((x - max) s) come
+// from two wave reductions.  They go to seg_m / seg_z for the draw, whose
+// weights on the bonus row are p alone: the segment sums then only need
+// rescaling to the row's final max, with no second pass over the row.  The
+// segments merge into the wave's state, returned uniform over the wave.
+template <int BT, int U, bool FAIR>
+__device__ __forceinline__ SmState stream_bonus(const char* trow, int64_t e0, int64_t e1, float s, float* seg_m,
+                                                float* seg_z)
+{
+    constexpr int NWV = BT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint4* vt = reinterpret_cast<const uint4*>(trow) + e0 / 8;
+    const int64_t nv = (e1 - e0) / 8;                  // whole vectors: e1 - e0 is a multiple of 8
+    const int nl = (int)((nv + 63) / 64);              // segments of the slice
+    const int niter = (nl + U * NWV - 1) / (U * NWV);
+    constexpr uint32_t NI = Fmt<SV_BF16>::NEG_INF_WORD;
+    SmState st = {NEG_INF, 0.f};
+    for (int it = 0; it < niter; ++it) {
+        if constexpr (FAIR) fair_priority(it, niter);
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = (int64_t)((it * U + u) * NWV + wave) * 64 + lane;
+            raw[u] = k < nv ? vt[k] : make_uint4(NI, NI, NI, NI);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int seg = (it * U + u) * NWV + wave;
+            if (seg < nl) {                            // uniform over the wave
+                float x[8];
+                unpack<SV_BF16>(raw[u], x);
+                const float wm = wave_max(tree_max<8>(x));
+                const float c = shift_of(wm, s);
+                float t[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
+                const float wz = wave_sum(tree_sum<8>(t));
+                if (lane == 0) {
+                    seg_m[seg] = wm;
+                    seg_z[seg] = wz;
+                }
+                st = sm_merge(st, {wm, wz}, s);
+            }
+        }
+    }
+    return st;
+}
+
 // DV: the draw's 16-byte pieces in flight per lane after a rejection at the
 // first position (GDV_EARLY with proposals, GDV_DEEP at K = 0).
 // LA: lookahead.  With LA = 0 a member streams position j only once j-1 is
@@ -1704,6 +1767,12 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const int tw = (GW - 1) * 64;                  // last wave loads the test inputs
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
 
+    // bonus row (position Kb) of a sampling sequence streamed in one pass with
+    // its segment sums (bf16 rows of whole vectors, no lookahead: there the
+    // bonus row is rarely reached and the path's registers would spill); set
+    // once it was
+    const bool seg_pass = !greedy && (V & 7) == 0;
+    bool bonus_segs = false;
     // s: last position streamed and published; d: last position settled
     // (both uniform over the workgroup).  Stream while at most LA positions
     // are streamed but unsettled, then settle the oldest.
@@ -1728,12 +1797,22 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                 // position 0: every sequence streams at once (fair share); later
                 // positions: the few long sequences, oldest-first is fine
                 const char* drow = dj ? draft_row<DTD>(P, b, j) : nullptr;
+                // the bonus row in one pass, its segment sums kept for the draw
+                const bool one = LA == 0 && DTT == SV_BF16 && j == Kb && seg_pass &&
+                                 (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
                 if (e0 < e1) {
-                    if (j == 0) stream_pair<DTT, DTD, GT, SU, true>(trow, drow, e0, e1, s, st, sd);
-                    else stream_pair<DTT, DTD, GT, SU>(trow, drow, e0, e1, s, st, sd);
+                    if (one) {
+                        if (j == 0) st = stream_bonus<GT, SU, true>(trow, e0, e1, s, seg_r, seg_p);
+                        else st = stream_bonus<GT, SU, false>(trow, e0, e1, s, seg_r, seg_p);
+                    } else if (j == 0) {
+                        stream_pair<DTT, DTD, GT, SU, true>(trow, drow, e0, e1, s, st, sd);
+                    } else {
+                        stream_pair<DTT, DTD, GT, SU>(trow, drow, e0, e1, s, st, sd);
+                    }
                 }
+                if (one) bonus_segs = true;
                 if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
-                st = wave_reduce_sm(st, s);
+                if (!one) st = wave_reduce_sm(st, s);      // the one-pass state is uniform already
                 if (dj) sd = wave_reduce_sm(sd, s);
                 if (lane == 0) {
                     sh_t[bi][wave] = st;
@@ -1836,7 +1915,14 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
     const bool fast_rows = t_al && (bonus || OH || d_al);
     __builtin_amdgcn_s_setprio(PRIO_DRAW);
-    if (bonus)
+    if (bonus && bonus_segs) {
+        // the segment sums of the one-pass stream, rescaled to the row's max
+        for (int l = tid; l < nl; l += GT) {
+            const float v = seg_p[l] * ex2(shift_of(seg_r[l], s) - cp);
+            seg_r[l] = v;
+            seg_p[l] = v;
+        }
+    } else if (bonus)
         draw_sums<DTT, DTD, OH, true, GDV_DEEP>(trow, drow, V, P.nseg, sg0, nl, s, cp, cq, w, ox, fast_rows, seg_r,
                                                 seg_p);
     else if (n == 0)
