@@ -1637,14 +1637,16 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     }
 }
 
-// The bonus row's slice of a sampling sequence in one pass (bf16 rows,
-// 16-byte aligned, whole vectors): load u of iteration it of wave w covers
-// exactly segment (it*U + u)*(BT/64) + w of the slice (64 lanes x 8
-// elements), so each segment's max and its sum of exp2((x - max) s) come
-// from two wave reductions.  They go to seg_m / seg_z for the draw, whose
-// weights on the bonus row are p alone: the segment sums then only need
-// rescaling to the row's final max, with no second pass over the row.  The
-// segments merge into the wave's state, returned uniform over the wave.
+// A row's slice in one pass with its segment sums (bf16 rows, 16-byte
+// aligned, whole vectors): load u of iteration it of wave w covers exactly
+// segment (it*U + u)*(BT/64) + w of the slice (64 lanes x 8 elements), so a
+// segment's sum is one wave reduction.  The exps are taken against a
+// wave-uniform reference, the first finite segment max, kept while the
+// segments' sums stay below 2^64 (fp32 sums are scale-invariant); a segment
+// that reaches it (an element far above, +Inf or NaN) takes its own max and
+// the reference moves there.  seg_m / seg_z get each segment's reference and
+// sum, so the draw can rescale them to the row's max instead of reading the
+// row again.  Returns the slice's state, uniform over the wave.
 template <int BT, int U, bool FAIR>
 __device__ __forceinline__ SmState stream_bonus(const char* trow, int64_t e0, int64_t e1, float s, float* seg_m,
                                                 float* seg_z)
@@ -1656,7 +1658,7 @@ __device__ __forceinline__ SmState stream_bonus(const char* trow, int64_t e0, in
     const int nl = (int)((nv + 63) / 64);              // segments of the slice
     const int niter = (nl + U * NWV - 1) / (U * NWV);
     constexpr uint32_t NI = Fmt<SV_BF16>::NEG_INF_WORD;
-    SmState st = {NEG_INF, 0.f};
+    SmState st = {NEG_INF, 0.f};                      // m: the reference while finite
     for (int it = 0; it < niter; ++it) {
         if constexpr (FAIR) fair_priority(it, niter);
         uint4 raw[U];
@@ -1669,19 +1671,35 @@ __device__ __forceinline__ SmState stream_bonus(const char* trow, int64_t e0, in
         for (int u = 0; u < U; ++u) {
             const int seg = (it * U + u) * NWV + wave;
             if (seg < nl) {                            // uniform over the wave
-                float x[8];
+                float x[8], t[8];
                 unpack<SV_BF16>(raw[u], x);
-                const float wm = wave_max(tree_max<8>(x));
-                const float c = shift_of(wm, s);
-                float t[8];
+                bool done = false;
+                if (st.m > NEG_INF && st.m < POS_INF) {
+                    const float c = st.m * s;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
-                const float wz = wave_sum(tree_sum<8>(t));
-                if (lane == 0) {
-                    seg_m[seg] = wm;
-                    seg_z[seg] = wz;
+                    for (int q = 0; q < 8; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
+                    const float wz = wave_sum(tree_sum<8>(t));
+                    if (wz < 0x1p64f) {                // uniform
+                        if (lane == 0) {
+                            seg_m[seg] = st.m;
+                            seg_z[seg] = wz;
+                        }
+                        st.z += wz;
+                        done = true;
+                    }
                 }
-                st = sm_merge(st, {wm, wz}, s);
+                if (!done) {                           // first finite segment, or the reference moves
+                    const float wm = vmax(wave_max(tree_max<8>(x)), st.m);
+                    const float c = shift_of(wm, s);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
+                    const float wz = wave_sum(tree_sum<8>(t));
+                    if (lane == 0) {
+                        seg_m[seg] = wm;
+                        seg_z[seg] = wz;
+                    }
+                    st = sm_merge(st, {wm, wz}, s);
+                }
             }
         }
     }
@@ -1767,12 +1785,12 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const int tw = (GW - 1) * 64;                  // last wave loads the test inputs
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
 
-    // bonus row (position Kb) of a sampling sequence streamed in one pass with
-    // its segment sums (bf16 rows of whole vectors, no lookahead: there the
-    // bonus row is rarely reached and the path's registers would spill); set
-    // once it was
+    // the bonus row (position Kb) of a sampling sequence streamed in one pass
+    // with its segment sums (bf16 rows of whole vectors, no lookahead: there
+    // the bonus row is rarely reached and the path's registers would spill);
+    // segs_pos is the position whose sums the LDS holds
     const bool seg_pass = !greedy && (V & 7) == 0;
-    bool bonus_segs = false;
+    int segs_pos = -1;
     // s: last position streamed and published; d: last position settled
     // (both uniform over the workgroup).  Stream while at most LA positions
     // are streamed but unsettled, then settle the oldest.
@@ -1810,7 +1828,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                         stream_pair<DTT, DTD, GT, SU>(trow, drow, e0, e1, s, st, sd);
                     }
                 }
-                if (one) bonus_segs = true;
+                if (one) segs_pos = j;
                 if (j == 0) __builtin_amdgcn_s_setprio(PRIO_CHAIN);
                 if (!one) st = wave_reduce_sm(st, s);      // the one-pass state is uniform already
                 if (dj) sd = wave_reduce_sm(sd, s);
@@ -1915,7 +1933,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     const bool d_al = drow != nullptr && (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
     const bool fast_rows = t_al && (bonus || OH || d_al);
     __builtin_amdgcn_s_setprio(PRIO_DRAW);
-    if (bonus && bonus_segs) {
+    if (bonus && segs_pos == n) {
         // the segment sums of the one-pass stream, rescaled to the row's max
         for (int l = tid; l < nl; l += GT) {
             const float v = seg_p[l] * ex2(shift_of(seg_r[l], s) - cp);
