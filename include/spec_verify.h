@@ -325,8 +325,8 @@ int spec_verify_lookup(const void* target_logits, int32_t dtype, const int32_t* 
  * order may settle a draw within rounding of a boundary differently):
  *   SV_MODE_AUTO  per call: SV_MODE_SEQ when position 0 alone streams at
  *                 least 64 MiB, or at least 16 MiB with K > 0, B <= 64 and
- *                 bf16 target logits, or for K = 0 on bf16 logits with V a
- *                 multiple of 8 (and the vocabulary fits its limit), else lazy
+ *                 bf16 target logits, or for K = 0 with V a multiple of 8
+ *                 (and the vocabulary fits its limit), else lazy
  *                 when one eager pass would stream at least 64 MiB of logits
  *                 per position (K+1 launches then pay off), else eager
  *   SV_MODE_EAGER one launch streams every row of every position

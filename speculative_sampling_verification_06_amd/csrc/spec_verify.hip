@@ -1637,49 +1637,60 @@ __device__ __forceinline__ void draw_sums(const char* trow, const char* drow, in
     }
 }
 
-// A row's slice in one pass with its segment sums (bf16 rows, 16-byte
-// aligned, whole vectors): load u of iteration it of wave w covers exactly
-// segment (it*U + u)*(BT/64) + w of the slice (64 lanes x 8 elements), so a
-// segment's sum is one wave reduction.  The exps are taken against a
-// wave-uniform reference, the first finite segment max, kept while the
-// segments' sums stay below 2^64 (fp32 sums are scale-invariant); a segment
-// that reaches it (an element far above, +Inf or NaN) takes its own max and
-// the reference moves there.  seg_m / seg_z get each segment's reference and
-// sum, so the draw can rescale them to the row's max instead of reading the
-// row again.  Returns the slice's state, uniform over the wave.
-template <int BT, int U, bool FAIR>
+// A row's slice in one pass with its segment sums (16-byte aligned rows of
+// whole vectors): a segment of 512 elements is VS = 512 / (64 * E) vectors
+// per lane of one wave (E elements per 16-byte vector: 1 for bf16, 2 for
+// fp32), lane l holding vectors l, l + 64, ... of the segment, and load
+// group u of iteration it of wave w covers segment (it*US + u)*(BT/64) + w
+// (US = U / VS groups), so a segment's sum is one wave reduction.  The exps
+// are taken against a wave-uniform reference, the first finite segment max,
+// kept while the segments' sums stay below 2^64 (fp32 sums are
+// scale-invariant); a segment that reaches it (an element far above, +Inf
+// or NaN) takes its own max and the reference moves there.  seg_m / seg_z
+// get each segment's reference and sum, so the draw can rescale them to the
+// row's max instead of reading the row again.  Returns the slice's state,
+// uniform over the wave.
+template <int DT, int BT, int U, bool FAIR>
 __device__ __forceinline__ SmState stream_bonus(const char* trow, int64_t e0, int64_t e1, float s, float* seg_m,
                                                 float* seg_z)
 {
+    constexpr int E = Fmt<DT>::E;                       // elements per 16-byte vector
+    constexpr int VS = SEG / (64 * E);                  // vectors per lane per segment
+    constexpr int US = (U + VS - 1) / VS;               // segments per lane and iteration
     constexpr int NWV = BT / 64;
+    constexpr int N = VS * E;                           // elements per lane per segment (8)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint4* vt = reinterpret_cast<const uint4*>(trow) + e0 / 8;
-    const int64_t nv = (e1 - e0) / 8;                  // whole vectors: e1 - e0 is a multiple of 8
-    const int nl = (int)((nv + 63) / 64);              // segments of the slice
-    const int niter = (nl + U * NWV - 1) / (U * NWV);
-    constexpr uint32_t NI = Fmt<SV_BF16>::NEG_INF_WORD;
-    SmState st = {NEG_INF, 0.f};                      // m: the reference while finite
+    const uint4* vt = reinterpret_cast<const uint4*>(trow) + e0 / E;
+    const int64_t nv = (e1 - e0) / E;                   // whole vectors: e1 - e0 is a multiple of 8
+    const int nl = (int)((e1 - e0 + SEG - 1) / SEG);    // segments of the slice
+    const int niter = (nl + US * NWV - 1) / (US * NWV);
+    constexpr uint32_t NI = Fmt<DT>::NEG_INF_WORD;
+    SmState st = {NEG_INF, 0.f};                       // m: the reference while finite
     for (int it = 0; it < niter; ++it) {
         if constexpr (FAIR) fair_priority(it, niter);
-        uint4 raw[U];
+        uint4 raw[US][VS];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = (int64_t)((it * U + u) * NWV + wave) * 64 + lane;
-            raw[u] = k < nv ? vt[k] : make_uint4(NI, NI, NI, NI);
+        for (int u = 0; u < US; ++u) {
+#pragma unroll
+            for (int v = 0; v < VS; ++v) {
+                const int64_t k = (int64_t)((it * US + u) * NWV + wave) * (64 * VS) + v * 64 + lane;
+                raw[u][v] = k < nv ? vt[k] : make_uint4(NI, NI, NI, NI);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int seg = (it * U + u) * NWV + wave;
-            if (seg < nl) {                            // uniform over the wave
-                float x[8], t[8];
-                unpack<SV_BF16>(raw[u], x);
+        for (int u = 0; u < US; ++u) {
+            const int seg = (it * US + u) * NWV + wave;
+            if (seg < nl) {                             // uniform over the wave
+                float x[N], t[N];
+#pragma unroll
+                for (int v = 0; v < VS; ++v) unpack<DT>(raw[u][v], x + v * E);
                 bool done = false;
                 if (st.m > NEG_INF && st.m < POS_INF) {
                     const float c = st.m * s;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
-                    const float wz = wave_sum(tree_sum<8>(t));
-                    if (wz < 0x1p64f) {                // uniform
+                    for (int q = 0; q < N; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
+                    const float wz = wave_sum(tree_sum<N>(t));
+                    if (wz < 0x1p64f) {                 // uniform
                         if (lane == 0) {
                             seg_m[seg] = st.m;
                             seg_z[seg] = wz;
@@ -1688,12 +1699,12 @@ __device__ __forceinline__ SmState stream_bonus(const char* trow, int64_t e0, in
                         done = true;
                     }
                 }
-                if (!done) {                           // first finite segment, or the reference moves
-                    const float wm = vmax(wave_max(tree_max<8>(x)), st.m);
+                if (!done) {                            // first finite segment, or the reference moves
+                    const float wm = vmax(wave_max(tree_max<N>(x)), st.m);
                     const float c = shift_of(wm, s);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
-                    const float wz = wave_sum(tree_sum<8>(t));
+                    for (int q = 0; q < N; ++q) t[q] = ex2(__builtin_fmaf(x[q], s, -c));
+                    const float wz = wave_sum(tree_sum<N>(t));
                     if (lane == 0) {
                         seg_m[seg] = wm;
                         seg_z[seg] = wz;
@@ -1786,7 +1797,7 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     if (tid >= tw && tid - tw <= K) ti[tid - tw] = load_test_in<DTT, DTD>(P, b, tid - tw, greedy);
 
     // the bonus row (position Kb) of a sampling sequence streamed in one pass
-    // with its segment sums (bf16 rows of whole vectors, no lookahead: there
+    // with its segment sums (rows of whole 16-byte vectors, no lookahead: there
     // the bonus row is rarely reached and the path's registers would spill);
     // segs_pos is the position whose sums the LDS holds
     const bool seg_pass = !greedy && (V & 7) == 0;
@@ -1816,12 +1827,11 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                 // positions: the few long sequences, oldest-first is fine
                 const char* drow = dj ? draft_row<DTD>(P, b, j) : nullptr;
                 // the bonus row in one pass, its segment sums kept for the draw
-                const bool one = LA == 0 && DTT == SV_BF16 && j == Kb && seg_pass &&
-                                 (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
+                const bool one = LA == 0 && j == Kb && seg_pass && (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
                 if (e0 < e1) {
                     if (one) {
-                        if (j == 0) st = stream_bonus<GT, SU, true>(trow, e0, e1, s, seg_r, seg_p);
-                        else st = stream_bonus<GT, SU, false>(trow, e0, e1, s, seg_r, seg_p);
+                        if (j == 0) st = stream_bonus<DTT, GT, SU, true>(trow, e0, e1, s, seg_r, seg_p);
+                        else st = stream_bonus<DTT, GT, SU, false>(trow, e0, e1, s, seg_r, seg_p);
                     } else if (j == 0) {
                         stream_pair<DTT, DTD, GT, SU, true>(trow, drow, e0, e1, s, st, sd);
                     } else {
@@ -2203,8 +2213,8 @@ static int lookahead_for(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t d
 // rejection read, draws overlapping other sequences' streams) wins once
 // position 0 alone streams at least 64 MiB, enough to fill the chip, and
 // with lookahead from 16 MiB for up to 64 sequences of bf16 rows when there
-// are positions to test, and for the sampling step (K = 0) on bf16 rows of
-// whole vectors; it needs the vocabulary's segment sums to fit in LDS.  Otherwise lazy mode,
+// are positions to test, and for the sampling step (K = 0) on rows of whole
+// vectors; it needs the vocabulary's segment sums to fit in LDS.  Otherwise lazy mode,
 // which pays one latency-bound launch per position (5-20 us each on
 // gfx950), wins once the eager stream is long against K+1 such launches: at
 // least 64 MiB of logits per position; else eager.
@@ -2235,11 +2245,12 @@ static Sched choose_sched(int32_t B, int32_t K, int32_t V, int32_t dtt, int32_t 
     // at B=256 over a 19008-token shard (45.7 against 45.8 us) nor for fp32
     // target rows (50 against 42-44 us)
     if (seq_ok && K > 0 && p0 >= mib64 / 4 && B <= 64 && dtt == SV_BF16) return SEQ;
-    // the sampling step on bf16 rows of whole 16-byte vectors: the
-    // per-sequence launch reads each row once (the bonus row's segment sums
-    // are kept for the draw) against twice for eager (V=152064, per call:
-    // B=1 11.1 against 14.5 us, B=64 18.5 against 22.2, B=128 19.9 against 32.2)
-    if (K == 0 && seq_ok && dtt == SV_BF16 && V % 8 == 0) return SEQ;
+    // the sampling step on rows of whole 16-byte vectors: the per-sequence
+    // launch reads each row once (the bonus row's segment sums are kept for
+    // the draw) against twice for eager (V=152064, per call, bf16 / fp32:
+    // B=1 10.6 / 11.4 against 15.1 / 14.2 us, B=64 19.0 / 20.5 against
+    // 22.1 / 25.9, B=256 22.2 / 31.0 against 46.6 / 58.2)
+    if (K == 0 && seq_ok && V % 8 == 0) return SEQ;
     if (K == 0) return EAGER;
     const double bytes = (double)B * V * ((double)(K + 1) * bt + (double)K * bd);
     return bytes >= (double)(K + 1) * mib64 ? LAZY : EAGER;

@@ -200,7 +200,7 @@ def test_schedule_query(lib):
         assert binding.schedule(64, 0, 128256, bf) == binding.MODE_SEQ            # K = 0, bf16: each row read once
         assert binding.schedule(1, 0, 152064, bf) == binding.MODE_SEQ
         assert binding.schedule(64, 0, 128257, bf) == binding.MODE_EAGER          # K = 0, not whole vectors
-        assert binding.schedule(64, 0, 128256, binding.SV_F32) == binding.MODE_EAGER   # K = 0, fp32 rows
+        assert binding.schedule(64, 0, 128256, binding.SV_F32) == binding.MODE_SEQ     # K = 0, fp32 rows
         assert binding.schedule(16, 5, 128256, bf) == binding.MODE_EAGER          # 7.8 MiB
         assert binding.schedule(64, 8, 2048 * 1024 + 1, bf) == binding.MODE_LAZY  # past the LDS limit
         for bad in ((1, 64, 10, bf), (1, 1, 0, bf), (-1, 1, 10, bf), (1, 1, 10, 7)):

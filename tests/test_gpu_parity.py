@@ -301,14 +301,15 @@ def test_schedules_ragged(dev, schedule, B, K, V, dtype, greedy_every, sd):
 
 @SCHED
 @pytest.mark.parametrize("V", [50000, 50003], ids=["whole_vectors", "ragged"])
-def test_schedules_every_proposal_accepted(dev, schedule, V):
+@pytest.mark.parametrize("dtype", [I.BF16, I.F32], ids=["bf16", "f32"])
+def test_schedules_every_proposal_accepted(dev, schedule, V, dtype):
     """Draft rows equal to the target rows (q = p): every test accepts, so every
     sequence draws its final token from the bonus row p_K (the per-sequence
     schedule streams that row once and keeps its segment sums when the row is
     whole 16-byte vectors; the ragged vocabulary takes the two-pass draw)."""
     B, K = 24, 4
-    w = I.synth_logits(5151, B, K, V, dtype=I.BF16, T=0.8, sigma=3.0, zipf=True, draft_scale=1.0,
-                       draft_sigma=1.0, name=f"all_accepted_{V}")
+    w = I.synth_logits(5151, B, K, V, dtype=dtype, T=0.8, sigma=3.0, zipf=True, draft_scale=1.0,
+                       draft_sigma=1.0, name=f"all_accepted_{V}_{I.DTYPE_NAMES[dtype]}")
     d = w.target[:, :K, :].copy()
     w2 = I.Workload(w.name, B, K, V, w.dtype, w.T, w.target, d, w.tokens, w.uniforms, w.greedy)
     g, o, rep = check(w2, dev)
