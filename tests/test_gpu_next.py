@@ -34,7 +34,7 @@ def _log(msg):
 @pytest.mark.parametrize("mode,groups", [(binding.MODE_AUTO, 0), (binding.MODE_SEQ, 0), (binding.MODE_SEQ, 1)],
                          ids=["auto", "seq", "seq1"])
 @pytest.mark.parametrize("B,V,dtype,T", [(64, 50000, I.BF16, 0.7), (7, 1001, I.F32, 1.3), (300, 152064, I.BF16, 1.0),
-                                         (5, 1, I.F32, 1.0)])
+                                         (5, 1, I.F32, 1.0), (48, 50000, I.F32, 0.9)])
 def test_sample_matches_oracle(dev, B, V, dtype, T, mode, groups):
     binding.set_mode(mode)
     binding.set_seq_groups(groups)
@@ -86,14 +86,43 @@ def test_sample_law_chi_square(dev):
     assert pv > S.ALPHA
 
 
-def test_sample_invalid_rows(dev):
+@pytest.mark.parametrize("mode", [binding.MODE_AUTO, binding.MODE_EAGER, binding.MODE_SEQ], ids=["auto", "eager", "seq"])
+@pytest.mark.parametrize("V", [100, 1024], ids=["ragged", "whole_vectors"])
+@pytest.mark.parametrize("dt", ["float32", "bfloat16"])
+def test_sample_invalid_rows(dev, mode, V, dt):
+    """Rows the draw cannot use mark only their own sequence (NaN, +Inf, all -Inf,
+    a uniform of 1); a row whose late segment holds a value far above the first
+    segment's (the one-pass reference moves) still draws like the oracle."""
     import torch
-    logits = torch.randn(4, 100, device=dev)
+    dtype = getattr(torch, dt)
+    g = torch.Generator().manual_seed(V)
+    logits = torch.randn(7, V, generator=g)
     logits[1, 5] = float("nan")
     logits[2] = float("-inf")
-    u = torch.tensor([0.5, 0.5, 0.5, 1.0], device=dev)
-    tok = binding.sample(logits, u, 1.0).cpu().numpy()
-    assert tok[0] >= 0 and list(tok[1:]) == [-1, -1, -1]
+    logits[4, V - 3] = float("inf")
+    logits[5, V - 1] = 200.0           # far above everything before it
+    logits[6, : V // 2] = float("-inf")
+    logits = logits.to(dtype).to(dev)
+    u = torch.tensor([0.5, 0.5, 0.5, 1.0, 0.5, 0.25, 0.75], device=dev)
+    binding.set_mode(mode)
+    try:
+        tok = binding.sample(logits, u, 1.0).cpu().numpy()
+    finally:
+        binding.set_mode(binding.MODE_AUTO)
+    assert list(tok[[1, 2, 3, 4]]) == [-1, -1, -1, -1]
+    assert tok[5] == V - 1              # the spike carries all the mass at fp32
+    host = logits.cpu()
+    if dt == "float32":
+        rows, code = host.numpy(), I.F32
+    else:
+        rows, code = host.view(torch.int16).numpy().view(np.uint16), I.BF16
+    B = rows.shape[0]
+    w = I.Workload(f"sample_invalid_{V}_{dt}", B, 0, V, code, 1.0, rows[:, None, :].copy(),
+                   np.empty((B, 0, V), rows.dtype), np.empty((B, 0), np.int32),
+                   u.cpu().numpy()[:, None].astype(np.float32), np.zeros(B, np.uint8))
+    o = oracle.verify(w)
+    g = {"accepted_len": np.where(tok >= 0, 0, -1).astype(np.int32), "out_tokens": tok[:, None]}
+    parity.compare(w, g, o, strict_diag=False)
 
 
 # --------------------------------------------------------------- KV commit --
