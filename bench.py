@@ -228,6 +228,38 @@ def _copy_calibration(args, torch, dev):
     del src, dst
 
 
+def hbm_ceiling(torch, np, binding, dev, mib=1024, reps=10):
+    """What plain streaming kernels reach on this GPU (sv_hbm_probe): a 1 GiB
+    read and a 1 GiB copy (read + write bytes), median over reps, HIP events
+    on the launch stream."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    words = binding.hbm_probe(binding.PROBE_READ, src)
+    out = {}
+    for name, fn, nbytes in (("read", lambda: binding.hbm_probe(binding.PROBE_READ, src, words), n * 4),
+                             ("copy", lambda: binding.hbm_probe(binding.PROBE_COPY, src, dst), 2 * n * 4)):
+        fn()
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        out[f"{name}_GBps"] = nbytes / (ms * 1e-3) / 1e9
+        out[f"{name}_ms"] = ms
+    out["bytes_read"] = n * 4
+    out["frac_of_peak"] = {"read": out["read_GBps"] / HBM_PEAK_GBS, "copy": out["copy_GBps"] / HBM_PEAK_GBS}
+    out["kernels"] = "sv_hbm_probe read and copy over 1 GiB (16-byte non-temporal accesses), median of 10"
+    del src, dst, words
+    torch.cuda.synchronize()
+    return out
+
+
 def bench_verify(args, torch, np, binding, I, dev, w=None, steps=None):
     w = I.CONFIGS[args.config]() if w is None else w
     steps = args.steps if steps is None else steps
@@ -598,6 +630,8 @@ def main() -> int:
             wl, gl, rl, kl = leg(args, torch, np, binding, I, dev, w=make(), steps=args.workload_steps)
             result["workloads"][name] = _summary(rl, _parity(np, wl, gl, kl))
             print(f"[bench] {name}: {result['workloads'][name]}", file=sys.stderr, flush=True)
+        result["hbm_ceiling"] = hbm_ceiling(torch, np, binding, dev)
+        print(f"[bench] hbm ceiling: {result['hbm_ceiling']}", file=sys.stderr, flush=True)
 
     print(json.dumps(result), flush=True)
     return 0

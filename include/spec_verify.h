@@ -403,6 +403,29 @@ int sv_seq_lookahead(int32_t B, int32_t K, int32_t V, int32_t target_dtype, int3
  * 0..2^20.                                                                */
 int sv_set_wait_limit(int32_t polls);
 
+/* ---- measurement aid: the HBM ceiling ---------------------------------
+ * Not part of the verify step.  The pages compare decoding methods by the
+ * memory traffic their kernels move ([QH] "Vấn đề thời gian"; [NL] "Tingkat
+ * penerimaan tidak sama dengan speedup"); these two plain streaming kernels
+ * measure the HBM rate this GPU reaches, the ceiling the verify kernels are
+ * judged against.
+ *
+ * sv_hbm_probe(SV_PROBE_READ, src, dst, bytes, stream): reads bytes from src
+ *   (16-byte non-temporal loads, eight 256-thread workgroups per compute
+ *   unit, grid-stride) and writes one 32-bit word per wave (an XOR of what it
+ *   read) to dst, which must hold sv_hbm_probe_words() words.
+ * sv_hbm_probe(SV_PROBE_COPY, src, dst, bytes, stream): copies bytes from
+ *   src to dst with the same loads and non-temporal stores.
+ * Device pointers, 16-byte aligned; bytes > 0 and a multiple of 16; the copy's
+ * ranges must not overlap.  Asynchronous on stream.  Returns SV_OK, SV_EINVAL
+ * (kind, pointers, size or overlap; nothing launched) or SV_ELAUNCH.
+ * sv_hbm_probe_words: the words the read writes on the current device, -1 if
+ * the device cannot be queried.                                           */
+#define SV_PROBE_READ 0
+#define SV_PROBE_COPY 1
+int sv_hbm_probe(int32_t kind, const void* src, void* dst, size_t bytes, void* stream);
+int32_t sv_hbm_probe_words(void);
+
 /* The HIP error code (hipError_t) behind this thread's most recent
  * SV_ELAUNCH, 0 if none yet.  Entry points clear an error left by an earlier
  * HIP call of the caller before launching, so SV_ELAUNCH always means one of

@@ -28,7 +28,8 @@ EXPORTS = ("sv_workspace_bytes", "spec_verify", "spec_verify_ex", "sv_stats", "s
            "sv_set_mode", "sv_get_mode", "sv_schedule", "sv_set_seq_groups", "sv_seq_groups", "sv_set_wait_limit",
            "sv_set_seq_lookahead", "sv_seq_lookahead",
            "sv_lookup_propose", "spec_verify_lookup", "sv_last_hip_error",
-           "spec_verify_noalloc", "sv_noalloc_scratch_bytes", "spec_verify_mode", "sv_strerror", "sv_version")
+           "spec_verify_noalloc", "sv_noalloc_scratch_bytes", "spec_verify_mode", "sv_strerror", "sv_version",
+           "sv_hbm_probe", "sv_hbm_probe_words")
 MODE_AUTO, MODE_EAGER, MODE_LAZY, MODE_SEQ = 0, 1, 2, 3
 
 
@@ -101,6 +102,10 @@ def load_library(path: str = LIB_PATH):
                                          C.c_int32, C.c_int32, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
             lib.sv_last_hip_error.restype = C.c_int
             lib.sv_last_hip_error.argtypes = []
+            lib.sv_hbm_probe.restype = C.c_int
+            lib.sv_hbm_probe.argtypes = [C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+            lib.sv_hbm_probe_words.restype = C.c_int32
+            lib.sv_hbm_probe_words.argtypes = []
             lib.sv_lookup_propose.restype = C.c_int
             lib.sv_lookup_propose.argtypes = [C.c_void_p, C.c_void_p] + [C.c_int32] * 5 + [C.c_void_p] * 3
             lib.spec_verify_lookup.restype = C.c_int
@@ -804,6 +809,35 @@ def kv_commit_in_place(cache_len, accepted_len, K, offset=1, l_max=None, status=
                                           status.data_ptr(), stream))
     return status
 
+
+
+PROBE_READ, PROBE_COPY = 0, 1
+
+
+def hbm_probe(kind, src, dst=None, stream=None):
+    """sv_hbm_probe: a plain streaming read (kind PROBE_READ; dst, if given,
+    holds sv_hbm_probe_words() int32 words) or copy (PROBE_COPY; dst like src)
+    over the whole of src, a contiguous device tensor.  Returns dst."""
+    torch = _torch()
+    _dev_ptr(src, "src")
+    nbytes = src.numel() * src.element_size()
+    lib = load_library()
+    if dst is None:
+        if kind == PROBE_READ:
+            words = int(lib.sv_hbm_probe_words())
+            if words < 1:
+                raise RuntimeError("sv_hbm_probe_words: device not queryable")
+            dst = torch.empty(words, dtype=torch.int32, device=src.device)
+        else:
+            dst = torch.empty_like(src)
+    _dev_ptr(dst, "dst")
+    need = 4 * int(lib.sv_hbm_probe_words()) if kind == PROBE_READ else nbytes
+    if dst.numel() * dst.element_size() < need:
+        raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, needs {need}")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    _check_rc(lib.sv_hbm_probe(kind, src.data_ptr(), dst.data_ptr(), nbytes, stream))
+    return dst
 
 
 class BoundSample:

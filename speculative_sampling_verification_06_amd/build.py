@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["spec_verify.hip", "lmhead.hip", "kvcache.hip", "lookup.hip"]
+SOURCES = ["spec_verify.hip", "lmhead.hip", "kvcache.hip", "lookup.hip", "hbm.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: hipcc must not emit v_pk_{add,mul,fma}_f32.

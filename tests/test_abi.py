@@ -274,3 +274,15 @@ def test_seq_lookahead_knob(lib):
     finally:
         lib.sv_set_mode(old)
         binding.set_seq_lookahead(-1)
+
+
+def test_hbm_probe_host_checks(lib):
+    """sv_hbm_probe refuses a bad kind, null or misaligned pointers, sizes that
+    are not whole 16-byte vectors and overlapping copies before launching (host
+    checks only: the dummy addresses are never dereferenced)."""
+    a, b = C.c_void_p(1 << 20), C.c_void_p(1 << 30)
+    bad = [(2, a, b, 4096), (-1, a, b, 4096), (binding.PROBE_READ, None, b, 4096), (binding.PROBE_COPY, a, None, 4096),
+           (binding.PROBE_READ, a, b, 0), (binding.PROBE_READ, a, b, 4100), (binding.PROBE_READ, C.c_void_p((1 << 20) + 8), b, 4096),
+           (binding.PROBE_COPY, a, C.c_void_p((1 << 20) + 4096), 8192)]
+    for kind, s, d, n in bad:
+        assert lib.sv_hbm_probe(kind, s, d, n, None) == binding.SV_EINVAL, (kind, s, d, n)

@@ -204,3 +204,22 @@ def test_kv_commit_without_entries(dev):
     assert ln.cpu().tolist() == [0, 3, 7, 16, 2]
     assert st.cpu().tolist() == [0, 0, 1, 0, 0]
     assert int(cache.sum()) == 0
+
+
+# --------------------------------------------------- HBM ceiling kernels --
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 3 * (1 << 20) + 16 * 37])
+def test_hbm_probe_reads_and_copies_everything(dev, nbytes):
+    """The read's per-wave words XOR to the XOR of every input word; the copy is exact."""
+    import torch
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    src = host.to(dev)
+    words = binding.hbm_probe(binding.PROBE_READ, src)
+    dst = binding.hbm_probe(binding.PROBE_COPY, src)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    w = words.cpu().numpy().view(np.uint32)
+    used = min(len(w), 4 * ((nbytes // 16 + 1023) // 1024))       # waves of the launched workgroups
+    assert np.bitwise_xor.reduce(w[:used]) == want
+    assert torch.equal(dst.cpu(), host)
