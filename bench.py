@@ -526,6 +526,8 @@ def main() -> int:
                     help="timed steps (hot and cache-flushed each) of every other named workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this size (for PMC byte scaling)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="print only the HBM ceiling (plain streaming read and copy) as one JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -550,6 +552,9 @@ def main() -> int:
                       "seq": binding.MODE_SEQ}[args.mode])
     binding.set_seq_groups(args.seq_groups)
     binding.set_seq_lookahead(args.seq_lookahead)
+    if args.ceiling_only:
+        print(json.dumps({"hbm_ceiling": hbm_ceiling(torch, np, binding, dev)}), flush=True)
+        return 0
 
     fn = {"lmhead": bench_lmhead, "sample": bench_sample, "kvcommit": bench_kvcommit,
           "lookup": bench_lookup}.get(args.config, bench_verify)
