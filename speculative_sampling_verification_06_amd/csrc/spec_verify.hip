@@ -1808,6 +1808,10 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
     // with lookahead the slices are small (few sequences): four loads per lane
     // and row cover a 16 KB slice in one round trip
     constexpr int SU = LA > 0 ? 4 : GU;
+    // the sampling step (K = 0; the only use of the deep-draw instance without
+    // lookahead) streams one row, not a pair: six loads per lane keep a pair's
+    // bytes in flight (V=152064 bf16, B=64: 19.0 -> 18.1 us; B=256 22.4 -> 22.2)
+    constexpr int SB = (DV == GDV_DEEP && LA == 0) ? 2 * GU : SU;
     int s_ = -1, d_ = -1;
     for (;;) {
         if (s_ < Ke && s_ - d_ <= LA) {
@@ -1830,8 +1834,8 @@ __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
                 const bool one = LA == 0 && j == Kb && seg_pass && (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
                 if (e0 < e1) {
                     if (one) {
-                        if (j == 0) st = stream_bonus<DTT, GT, SU, true>(trow, e0, e1, s, seg_r, seg_p);
-                        else st = stream_bonus<DTT, GT, SU, false>(trow, e0, e1, s, seg_r, seg_p);
+                        if (j == 0) st = stream_bonus<DTT, GT, SB, true>(trow, e0, e1, s, seg_r, seg_p);
+                        else st = stream_bonus<DTT, GT, SB, false>(trow, e0, e1, s, seg_r, seg_p);
                     } else if (j == 0) {
                         stream_pair<DTT, DTD, GT, SU, true>(trow, drow, e0, e1, s, st, sd);
                     } else {
