@@ -635,6 +635,23 @@ def main() -> int:
             wl, gl, rl, kl = leg(args, torch, np, binding, I, dev, w=make(), steps=args.workload_steps)
             result["workloads"][name] = _summary(rl, _parity(np, wl, gl, kl))
             print(f"[bench] {name}: {result['workloads'][name]}", file=sys.stderr, flush=True)
+        # the NEXT rows (sampling step, KV commit, prompt lookup + its verify), fewer steps each
+        import copy
+        a2 = copy.copy(args)
+        a2.steps, a2.settle_ms = args.workload_steps, 50.0
+        result["next_rows"] = {}
+        for name, leg in (("sample", bench_sample), ("kvcommit", bench_kvcommit), ("lookup", bench_lookup)):
+            wl, gl, rl, kl = leg(a2, torch, np, binding, I, dev)
+            rf = rl["roofline"]
+            entry = {"workload": rl["config"]["workload"], "ms_per_step": rl["ms_per_step"], "value": rl["value"],
+                     "unit": rl["unit"], "kernel": rf["kernel"], "algorithmic_bytes": rf["algorithmic_bytes_per_launch"],
+                     "avg_launch_ms": rf["avg_launch_ms"], "achieved_GBs": rf["achieved"], "roofline_frac": rf["frac"]}
+            if "hot" in rl:
+                entry["hot_ms_per_step"] = rl["hot"]["ms_per_step"]
+            if kl == "sample":
+                entry["parity"] = _parity(np, wl, gl, kl)
+            result["next_rows"][name] = entry
+            print(f"[bench] {name}: {entry}", file=sys.stderr, flush=True)
         result["hbm_ceiling"] = hbm_ceiling(torch, np, binding, dev)
         print(f"[bench] hbm ceiling: {result['hbm_ceiling']}", file=sys.stderr, flush=True)
 
