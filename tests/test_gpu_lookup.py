@@ -52,6 +52,21 @@ def test_propose_random_histories(dev, alphabet, n_max, n_min, K):
     _log(f"[lookup] alphabet={alphabet} n={n_min}..{n_max} K={K}: klen hist {np.bincount(ko, minlength=K + 1).tolist()}")
 
 
+@pytest.mark.parametrize("Lmax", [15360, 15361], ids=["staged_in_lds", "global_memory"])
+def test_propose_histories_at_the_lds_limit(dev, Lmax):
+    """Histories of up to 15360 tokens are compared in LDS, longer ones in
+    global memory: both agree with the oracle at the boundary, with the
+    earliest occurrence of the longest ending far from the end."""
+    rng = np.random.default_rng(Lmax)
+    B = 4
+    h = rng.integers(0, 3, size=(B, Lmax)).astype(np.int32)
+    h[:, 40:48] = h[:, Lmax - 8:Lmax]                  # the whole 8-token ending once near the start
+    ln = np.array([Lmax, Lmax - 1, Lmax // 2, 2], np.int32)
+    cg, kg = _propose_gpu(dev, h, ln, 8, 1, 6)
+    co, ko = lookup.propose(h, ln, 8, 1, 6)
+    assert np.array_equal(kg, ko) and np.array_equal(cg, co)
+
+
 def test_propose_invalid_lengths_and_empty(dev):
     h = np.tile(np.array([[5, 6, 5, 6, 5]], np.int32), (4, 1))
     cg, kg = _propose_gpu(dev, h, np.array([-3, 6, 5, 0]), 2, 1, 4)
