@@ -1,6 +1,7 @@
 """GPU parity of the NEXT rows: the draft-side sampling step (sv_sample) and the
 KV-cache commit (sv_kv_commit), each against its oracle on the CPU."""
 
+import copy
 import os
 import sys
 
@@ -62,6 +63,46 @@ def _sample_case(dev, B, V, dtype, T):
     samp = (mask == 0) & (o.accepted_len >= 0)
     assert np.allclose(lse[samp], o.lse_p[samp, 0], rtol=1e-5, atol=1e-5)
     assert np.all(np.isnan(lse[mask == 1]))
+
+
+@pytest.mark.parametrize("dtype", [I.BF16, I.F32], ids=["bf16", "f32"])
+def test_sample_graph_replays_match_calls(dev, dtype):
+    """The sampling step (per-sequence launch, one pass over each row) captured
+    in a HIP graph on a side stream and replayed four times, the uniforms
+    rewritten before each replay and an uncaptured call in between: every
+    replay equals that call bit for bit and agrees with the oracle."""
+    import torch
+    B, V = 48, 50000
+    w = I.synth_logits(9200, B, 0, V, dtype=dtype, T=0.9, sigma=3.0, zipf=True, draft_scale=1.0, draft_sigma=1.0,
+                       name="sample_graph")
+    d = binding.to_device(w, dev)
+    logits = d["target"][:, 0, :].contiguous()
+    u = d["uniforms"][:, 0].contiguous()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call = binding.BoundSample(logits, u, w.T, stream=side.cuda_stream)
+        for _ in range(3):
+            call()
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(78)
+    for rep in range(4):
+        uu = I.grid_uniforms(rng, (B,)) if rep else w.uniforms[:, 0]
+        u.copy_(torch.from_numpy(np.ascontiguousarray(uu, np.float32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = call.tokens.cpu().numpy().copy()
+        ref = binding.sample(logits, u, w.T).cpu().numpy()   # uncaptured work between the replays
+        assert np.array_equal(got, ref), rep
+        wr = copy.copy(w)
+        wr.uniforms = np.asarray(uu, np.float32)[:, None]
+        g = {"accepted_len": np.where(got >= 0, 0, -1).astype(np.int32), "out_tokens": got[:, None]}
+        _log(f"[sample graph] replay {rep}: {parity.compare(wr, g, oracle.verify(wr), strict_diag=False)}")
 
 
 def test_sample_law_chi_square(dev):
