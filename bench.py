@@ -654,6 +654,14 @@ def main() -> int:
             print(f"[bench] {name}: {entry}", file=sys.stderr, flush=True)
         result["hbm_ceiling"] = hbm_ceiling(torch, np, binding, dev)
         print(f"[bench] hbm ceiling: {result['hbm_ceiling']}", file=sys.stderr, flush=True)
+        # every kernel's rate against what a plain read (a copy, for the KV commit) reaches in this run
+        rd, cp = result["hbm_ceiling"]["read_GBps"], result["hbm_ceiling"]["copy_GBps"]
+        result["roofline"]["frac_of_read_ceiling"] = result["roofline"]["achieved"] / rd
+        for v in result["workloads"].values():
+            v["frac_of_read_ceiling"] = v["achieved_GBs"] / rd
+        for k, v in result["next_rows"].items():
+            v["frac_of_copy_ceiling" if k == "kvcommit" else "frac_of_read_ceiling"] = \
+                v["achieved_GBs"] / (cp if k == "kvcommit" else rd)
 
     print(json.dumps(result), flush=True)
     return 0
