@@ -311,7 +311,9 @@ def bench_verify(args, torch, np, binding, I, dev, w=None, steps=None):
                         "hot_draw_median": float(np.median(t["hot_per"][1]))}
     res["method"] = _method_stats(w, acc)
     needed = I.needed_bytes(w, acc)
-    res["method"].update(needed_bytes=needed, eager_bytes=eager, useful_bytes_fraction=needed / eager)
+    # the compulsory-eager rate: the bytes an eager verify moves, over the step time
+    res["method"].update(needed_bytes=needed, eager_bytes=eager, useful_bytes_fraction=needed / eager,
+                         eager_equivalent_GBs=eager / (res["ms_per_step"] * 1e-3) / 1e9)
     return w, gpu, res, None
 
 
