@@ -213,6 +213,10 @@ __global__ __launch_bounds__(NT, WPS) void k_lmhead(const uint16_t* __restrict__
                 bf16x8 af[2][MT];
 #pragma unroll
                 for (int t = 0; t < MT; ++t) af[0][t] = *reinterpret_cast<const bf16x8*>(as + t * 32 * A_LD);
+                // all six reads go out before the first k-step's matrix ops: left
+                // to itself the scheduler sank them into one register set, each
+                // read then waiting on its own (GEMM 234-238 -> 228-229 us)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int step = kb * KS + ks;
